@@ -1,0 +1,226 @@
+"""ctypes binding of libdsa.so: argument marshalling only (no compute, no fallback).
+
+Tensors are torch device tensors; the HIP stream is torch's current stream unless one is
+given. Every call raises DsaError with the library's message when the C call fails.
+bf16 tensors are torch.bfloat16; fp8 E4M3FN tensors are torch.uint8 (raw bytes) or
+torch.float8_e4m3fn.
+"""
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(HERE, "libdsa.so")
+
+DSA_F32, DSA_BF16, DSA_FP8_E4M3 = 0, 1, 2
+IN_SEQ, ROUND_ROBIN = 0, 1
+
+c_i32, c_i64, c_p, c_f32, c_size = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_size_t
+
+
+class DsaError(RuntimeError):
+    pass
+
+
+class IndexerArgs(ctypes.Structure):
+    _fields_ = [
+        ("q_idx", c_p), ("q_scale", c_p), ("weights", c_p), ("k_idx", c_p), ("k_scale", c_p),
+        ("dtype", c_i32), ("nq", c_i32), ("nk", c_i32), ("n_heads", c_i32), ("head_dim", c_i32), ("batch", c_i32),
+        ("cu_seqlens_q", c_p), ("seqused_kv", c_p), ("cu_seqlens_kv", c_p),
+        ("max_seqlen_kv", c_i32), ("q_stride", c_i32), ("compress_ratio", c_i32), ("topk", c_i32),
+        ("kv_row_base", c_i32), ("window", c_i32), ("window_kv_start", c_p), ("topk_idx", c_p),
+        ("workspace", c_p), ("workspace_bytes", c_size), ("err_flag", c_p),
+    ]
+
+
+class AttnArgs(ctypes.Structure):
+    _fields_ = [
+        ("q", c_p), ("kv", c_p), ("idx", c_p), ("sink", c_p), ("out", c_p), ("lse", c_p), ("err_flag", c_p),
+        ("softmax_scale", c_f32), ("dtype", c_i32), ("nq", c_i32), ("n_rows", c_i32), ("n_heads", c_i32),
+        ("d_qk", c_i32), ("d_v", c_i32), ("k_tot", c_i32),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libdsa.so; raises if it has not been built (there is no fallback path)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise DsaError(f"{library_path} is missing: build it with `python -m sparse_attention_prefill_amd.build`")
+        L = ctypes.CDLL(library_path)
+        L.dsa_last_error.restype = ctypes.c_char_p
+        L.dsa_version.restype = ctypes.c_char_p
+        L.dsa_cp_sizes.argtypes = [c_i32] * 5 + [ctypes.POINTER(c_i32)] * 3
+        L.dsa_build_cp_metadata.argtypes = [c_p, c_p] + [c_i32] * 6 + [c_p] * 7
+        L.dsa_indexer_topk_workspace.argtypes = [ctypes.POINTER(IndexerArgs)]
+        L.dsa_indexer_topk_workspace.restype = c_size
+        L.dsa_indexer_topk.argtypes = [ctypes.POINTER(IndexerArgs), c_p]
+        L.dsa_indexer_scores.argtypes = [ctypes.POINTER(IndexerArgs), c_p, c_i64, c_p]
+        L.dsa_topk_from_scores.argtypes = [ctypes.POINTER(IndexerArgs), c_p, c_i64, c_p]
+        L.dsa_sparse_attn.argtypes = [ctypes.POINTER(AttnArgs), c_p]
+        L.dsa_rerange.argtypes = [c_p, c_p, c_i32, c_i64, c_i32, c_i32, c_i32, c_i32, c_p]
+        for f in ("dsa_cp_sizes", "dsa_build_cp_metadata", "dsa_indexer_topk", "dsa_indexer_scores",
+                  "dsa_topk_from_scores", "dsa_sparse_attn", "dsa_rerange"):
+            getattr(L, f).restype = c_i32
+        _lib = L
+    return _lib
+
+
+def version():
+    return lib().dsa_version().decode()
+
+
+def _check(status, what):
+    if status != 0:
+        raise DsaError(f"{what} failed ({status}): {lib().dsa_last_error().decode()}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return DSA_F32
+    if t.dtype == torch.bfloat16:
+        return DSA_BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return DSA_FP8_E4M3
+    raise DsaError(f"unsupported dtype {t.dtype}")
+
+
+def _mode(mode):
+    return {"in_seq": IN_SEQ, "round_robin": ROUND_ROBIN, IN_SEQ: IN_SEQ, ROUND_ROBIN: ROUND_ROBIN}[mode]
+
+
+def cp_sizes(num_tokens, cp_size, cp_rank, mode, pad_to_cp):
+    """(tokens_per_rank, n_local_real, num_rows_concat) of a rank (host only)."""
+    a, b, c = c_i32(), c_i32(), c_i32()
+    _check(lib().dsa_cp_sizes(num_tokens, cp_size, cp_rank, _mode(mode), int(pad_to_cp), ctypes.byref(a),
+                              ctypes.byref(b), ctypes.byref(c)), "dsa_cp_sizes")
+    return a.value, b.value, c.value
+
+
+def build_cp_metadata(query_start_loc, seq_lens, num_tokens, cp_size, cp_rank, mode, pad_to_cp=False,
+                      token_map=True, err_flag=None, stream=None):
+    """Run the metadata kernel; returns a dict of int32 device tensors."""
+    dev = query_start_loc.device
+    B = seq_lens.numel()
+    tpr, _, _ = cp_sizes(num_tokens, cp_size, cp_rank, mode, pad_to_cp)
+    out = {
+        "local_query_start_loc": torch.empty(B + 1, dtype=torch.int32, device=dev),
+        "local_seq_lens": torch.empty(max(B, 1), dtype=torch.int32, device=dev),
+        "local_kv_start_loc": torch.empty(B + 1, dtype=torch.int32, device=dev),
+        "scalars": torch.empty(8, dtype=torch.int32, device=dev),
+        "token_map": torch.empty(max(tpr, 1), dtype=torch.int32, device=dev) if token_map else None,
+    }
+    _check(lib().dsa_build_cp_metadata(
+        _ptr(query_start_loc), _ptr(seq_lens), B, num_tokens, cp_size, cp_rank, _mode(mode), int(pad_to_cp),
+        _ptr(out["local_query_start_loc"]), _ptr(out["local_seq_lens"]), _ptr(out["local_kv_start_loc"]),
+        _ptr(out["scalars"]), _ptr(out["token_map"]), _ptr(err_flag), _stream(stream)), "dsa_build_cp_metadata")
+    out["local_seq_lens"] = out["local_seq_lens"][:B]
+    if token_map:
+        out["token_map"] = out["token_map"][:tpr]
+    return out
+
+
+def _indexer_args(q_idx, weights, k_idx, cu_seqlens_q, seqused_kv, cu_seqlens_kv, max_seqlen_kv, q_stride=1,
+                  compress_ratio=1, topk=2048, kv_row_base=0, window=0, window_kv_start=None, q_scale=None,
+                  k_scale=None, topk_idx=None, workspace=None, err_flag=None):
+    a = IndexerArgs()
+    a.q_idx, a.q_scale, a.weights = _ptr(q_idx), _ptr(q_scale), _ptr(weights)
+    a.k_idx, a.k_scale = _ptr(k_idx), _ptr(k_scale)
+    a.dtype = _dtype_code(q_idx)
+    a.nq, a.n_heads, a.head_dim = q_idx.shape[0], q_idx.shape[1], q_idx.shape[2]
+    a.nk = k_idx.shape[0]
+    a.batch = seqused_kv.numel()
+    a.cu_seqlens_q, a.seqused_kv, a.cu_seqlens_kv = _ptr(cu_seqlens_q), _ptr(seqused_kv), _ptr(cu_seqlens_kv)
+    a.max_seqlen_kv, a.q_stride, a.compress_ratio = int(max_seqlen_kv), int(q_stride), int(compress_ratio)
+    a.topk, a.kv_row_base, a.window = int(topk), int(kv_row_base), int(window)
+    a.window_kv_start, a.topk_idx = _ptr(window_kv_start), _ptr(topk_idx)
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    a.err_flag = _ptr(err_flag)
+    return a
+
+
+def indexer_topk_workspace(q_idx, weights, k_idx, cu_seqlens_q, seqused_kv, cu_seqlens_kv, max_seqlen_kv, **kw):
+    a = _indexer_args(q_idx, weights, k_idx, cu_seqlens_q, seqused_kv, cu_seqlens_kv, max_seqlen_kv, **kw)
+    n = lib().dsa_indexer_topk_workspace(ctypes.byref(a))
+    if n == 0:
+        raise DsaError(lib().dsa_last_error().decode())
+    return n
+
+
+def indexer_topk(q_idx, weights, k_idx, cu_seqlens_q, seqused_kv, cu_seqlens_kv, max_seqlen_kv, topk_idx=None,
+                 workspace=None, stream=None, **kw):
+    """Indexer scores + top-k into topk_idx [nq, topk + window] (allocated if not given)."""
+    topk = kw.get("topk", 2048)
+    window = kw.get("window", 0)
+    if topk_idx is None:
+        topk_idx = torch.empty(q_idx.shape[0], topk + window, dtype=torch.int32, device=q_idx.device)
+    if workspace is None:
+        n = indexer_topk_workspace(q_idx, weights, k_idx, cu_seqlens_q, seqused_kv, cu_seqlens_kv, max_seqlen_kv, **kw)
+        workspace = torch.empty(n, dtype=torch.uint8, device=q_idx.device)
+    a = _indexer_args(q_idx, weights, k_idx, cu_seqlens_q, seqused_kv, cu_seqlens_kv, max_seqlen_kv,
+                      topk_idx=topk_idx, workspace=workspace, **kw)
+    _check(lib().dsa_indexer_topk(ctypes.byref(a), _stream(stream)), "dsa_indexer_topk")
+    return topk_idx
+
+
+def indexer_scores(q_idx, weights, k_idx, cu_seqlens_q, seqused_kv, cu_seqlens_kv, max_seqlen_kv, scores,
+                   stream=None, **kw):
+    a = _indexer_args(q_idx, weights, k_idx, cu_seqlens_q, seqused_kv, cu_seqlens_kv, max_seqlen_kv, **kw)
+    _check(lib().dsa_indexer_scores(ctypes.byref(a), _ptr(scores), scores.stride(0), _stream(stream)),
+           "dsa_indexer_scores")
+    return scores
+
+
+def topk_from_scores(q_idx, weights, k_idx, cu_seqlens_q, seqused_kv, cu_seqlens_kv, max_seqlen_kv, scores,
+                     topk_idx=None, stream=None, **kw):
+    topk = kw.get("topk", 2048)
+    window = kw.get("window", 0)
+    if topk_idx is None:
+        topk_idx = torch.empty(q_idx.shape[0], topk + window, dtype=torch.int32, device=scores.device)
+    a = _indexer_args(q_idx, weights, k_idx, cu_seqlens_q, seqused_kv, cu_seqlens_kv, max_seqlen_kv,
+                      topk_idx=topk_idx, **kw)
+    _check(lib().dsa_topk_from_scores(ctypes.byref(a), _ptr(scores), scores.stride(0), _stream(stream)),
+           "dsa_topk_from_scores")
+    return topk_idx
+
+
+def sparse_attn(q, kv, idx, sink, softmax_scale, d_v, out=None, lse=None, err_flag=None, stream=None):
+    """Sparse attention of q [nq, H, D_qk] over kv rows idx [nq, k_tot]; returns out [nq, H, d_v]."""
+    nq, H, Dqk = q.shape
+    if out is None:
+        out = torch.empty(nq, H, d_v, dtype=q.dtype, device=q.device)
+    a = AttnArgs()
+    a.q, a.kv, a.idx, a.sink, a.out, a.lse, a.err_flag = (_ptr(q), _ptr(kv), _ptr(idx), _ptr(sink), _ptr(out),
+                                                          _ptr(lse), _ptr(err_flag))
+    a.softmax_scale = float(softmax_scale)
+    a.dtype = _dtype_code(q)
+    a.nq, a.n_rows, a.n_heads, a.d_qk, a.d_v = nq, kv.shape[0], H, Dqk, d_v
+    a.k_tot = idx.shape[1] if idx is not None else 0
+    _check(lib().dsa_sparse_attn(ctypes.byref(a), _stream(stream)), "dsa_sparse_attn")
+    return out
+
+
+def rerange(x, num_tokens, cp_size, mode, pad_to_cp, inverse=False, out=None, stream=None):
+    """Rank-concatenated rows -> logical order (inverse=False), or the split (inverse=True)."""
+    _, _, rows_concat = cp_sizes(num_tokens, cp_size, 0, mode, pad_to_cp)
+    n_out = rows_concat if inverse else num_tokens
+    if out is None:
+        out = torch.empty((n_out,) + tuple(x.shape[1:]), dtype=x.dtype, device=x.device)
+    row_bytes = x[0].numel() * x.element_size() if x.shape[0] else out[0].numel() * out.element_size()
+    _check(lib().dsa_rerange(_ptr(x), _ptr(out), num_tokens, row_bytes, cp_size, _mode(mode), int(pad_to_cp),
+                             int(inverse), _stream(stream)), "dsa_rerange")
+    return out

@@ -1,0 +1,194 @@
+// Host entry points of libdsa: argument checks, sizes and kernel dispatch. See include/dsa.h.
+#include <string.h>
+
+#include <string>
+
+#include "dsa_internal.h"
+
+namespace dsa {
+
+static thread_local std::string g_last_error;
+
+void set_error(const std::string& msg) { g_last_error = msg; }
+void clear_error() { g_last_error.clear(); }
+dsa_status fail(dsa_status code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+dsa_status check_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(DSA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  return DSA_OK;
+}
+
+dsa_status launch_cp_metadata(const int32_t*, const int32_t*, int, int, int, int, int, int32_t*, int32_t*, int32_t*,
+                              int32_t*, int32_t*, int32_t*, hipStream_t);
+dsa_status launch_rerange(const void*, void*, int, int64_t, int, int, int, int, int, hipStream_t);
+dsa_status launch_indexer_scores(const dsa_indexer_topk_args*, float*, int64_t, int, hipStream_t);
+dsa_status launch_topk(const dsa_indexer_topk_args*, const float*, int64_t, int, hipStream_t);
+dsa_status launch_sparse_attn(const dsa_sparse_attn_args*, hipStream_t);
+
+namespace {
+
+bool valid_mode(int32_t m) { return m == DSA_SPLIT_IN_SEQ || m == DSA_SPLIT_ROUND_ROBIN; }
+
+// visible keys of the longest row, and the float32 score-row stride
+int max_visible(const dsa_indexer_topk_args* a) {
+  return a->compress_ratio > 1 ? a->max_seqlen_kv / a->compress_ratio : a->max_seqlen_kv;
+}
+int64_t score_ld(const dsa_indexer_topk_args* a) {
+  const int64_t mv = max_visible(a) > 0 ? max_visible(a) : 1;
+  return (mv + 63) / 64 * 64;
+}
+
+dsa_status check_indexer_args(const dsa_indexer_topk_args* a, bool need_out) {
+  if (!a) return fail(DSA_ERR_INVALID_ARG, "indexer: args is NULL");
+  if (a->nq < 0 || a->nk < 0 || a->batch < 0 || a->n_heads < 1 || a->head_dim < 1)
+    return fail(DSA_ERR_INVALID_ARG, "indexer: negative or zero size");
+  if (a->topk < 1) return fail(DSA_ERR_INVALID_ARG, "indexer: topk must be >= 1");
+  if (a->window < 0) return fail(DSA_ERR_INVALID_ARG, "indexer: window must be >= 0");
+  if (a->q_stride < 1) return fail(DSA_ERR_INVALID_ARG, "indexer: q_stride must be >= 1");
+  if (a->compress_ratio < 1) return fail(DSA_ERR_INVALID_ARG, "indexer: compress_ratio must be >= 1");
+  if (a->max_seqlen_kv < 0) return fail(DSA_ERR_INVALID_ARG, "indexer: max_seqlen_kv must be >= 0");
+  if (a->dtype != DSA_F32 && a->dtype != DSA_BF16 && a->dtype != DSA_FP8_E4M3)
+    return fail(DSA_ERR_UNSUPPORTED, "indexer: unknown dtype");
+  if (a->nq == 0) return DSA_OK;
+  if (a->batch < 1) return fail(DSA_ERR_INVALID_ARG, "indexer: batch must be >= 1 when nq > 0");
+  if (!a->q_idx || !a->weights || !a->cu_seqlens_q || !a->seqused_kv || !a->cu_seqlens_kv)
+    return fail(DSA_ERR_INVALID_ARG, "indexer: NULL input pointer");
+  if (a->nk > 0 && !a->k_idx) return fail(DSA_ERR_INVALID_ARG, "indexer: NULL k_idx");
+  if (a->dtype == DSA_FP8_E4M3 && (!a->q_scale || !a->k_scale))
+    return fail(DSA_ERR_INVALID_ARG, "indexer: fp8 needs q_scale and k_scale");
+  if (need_out && !a->topk_idx) return fail(DSA_ERR_INVALID_ARG, "indexer: NULL topk_idx");
+  if (a->window > 0 && !a->window_kv_start) return fail(DSA_ERR_INVALID_ARG, "indexer: window needs window_kv_start");
+  if (!aligned16(a->q_idx) || (a->k_idx && !aligned16(a->k_idx)))
+    return fail(DSA_ERR_INVALID_ARG, "indexer: q_idx / k_idx must be 16-byte aligned");
+  if (max_visible(a) > 131072) return fail(DSA_ERR_UNSUPPORTED, "indexer: more than 131072 visible keys per row");
+  const bool mfma = a->n_heads == 64 && a->head_dim == 128;
+  if (a->dtype == DSA_FP8_E4M3 && !mfma) return fail(DSA_ERR_UNSUPPORTED, "indexer: fp8 needs 64 heads x 128");
+  return DSA_OK;
+}
+
+}  // namespace
+}  // namespace dsa
+
+using namespace dsa;
+
+extern "C" {
+
+const char* dsa_last_error(void) { return g_last_error.c_str(); }
+
+const char* dsa_version(void) { return "dsa-mi355x 0.1 (gfx950)"; }
+
+dsa_status dsa_cp_sizes(int32_t num_tokens, int32_t cp_size, int32_t cp_rank, int32_t mode, int32_t pad_to_cp,
+                        int32_t* tokens_per_rank, int32_t* n_local_real, int32_t* num_rows_concat) {
+  clear_error();
+  if (num_tokens < 0 || cp_size < 1 || cp_rank < 0 || cp_rank >= cp_size)
+    return fail(DSA_ERR_INVALID_ARG, "cp_sizes: need num_tokens >= 0 and 0 <= cp_rank < cp_size");
+  if (!valid_mode(mode)) return fail(DSA_ERR_INVALID_ARG, "cp_sizes: unknown split mode");
+  const int64_t tpr = (int64_t(num_tokens) + cp_size - 1) / cp_size;
+  int64_t real;
+  if (mode == DSA_SPLIT_ROUND_ROBIN) real = num_tokens > cp_rank ? (num_tokens - cp_rank + cp_size - 1) / cp_size : 0;
+  else real = std::max<int64_t>(0, std::min<int64_t>((cp_rank + 1) * tpr, num_tokens) - std::min<int64_t>(cp_rank * tpr, num_tokens));
+  if (tokens_per_rank) *tokens_per_rank = int32_t(tpr);
+  if (n_local_real) *n_local_real = int32_t(real);
+  if (num_rows_concat) *num_rows_concat = pad_to_cp ? int32_t(tpr * cp_size) : num_tokens;
+  return DSA_OK;
+}
+
+dsa_status dsa_build_cp_metadata(const int32_t* query_start_loc, const int32_t* seq_lens, int32_t batch,
+                                 int32_t num_tokens, int32_t cp_size, int32_t cp_rank, int32_t mode, int32_t pad_to_cp,
+                                 int32_t* local_query_start_loc, int32_t* local_seq_lens, int32_t* local_kv_start_loc,
+                                 int32_t* scalars, int32_t* token_map, int32_t* err_flag, void* stream) {
+  clear_error();
+  (void)pad_to_cp;
+  if (batch < 0 || num_tokens < 0) return fail(DSA_ERR_INVALID_ARG, "cp_metadata: negative batch or num_tokens");
+  if (cp_size < 1 || cp_rank < 0 || cp_rank >= cp_size)
+    return fail(DSA_ERR_INVALID_ARG, "cp_metadata: need 0 <= cp_rank < cp_size");
+  if (!valid_mode(mode)) return fail(DSA_ERR_INVALID_ARG, "cp_metadata: unknown split mode");
+  if (!query_start_loc || !local_query_start_loc || !local_kv_start_loc || !scalars ||
+      (batch > 0 && (!seq_lens || !local_seq_lens)))
+    return fail(DSA_ERR_INVALID_ARG, "cp_metadata: NULL pointer");
+  return launch_cp_metadata(query_start_loc, seq_lens, batch, num_tokens, cp_size, cp_rank, mode,
+                            local_query_start_loc, local_seq_lens, local_kv_start_loc, scalars, token_map, err_flag,
+                            as_stream(stream));
+}
+
+size_t dsa_indexer_topk_workspace(const dsa_indexer_topk_args* a) {
+  clear_error();
+  if (check_indexer_args(a, false) != DSA_OK) return 0;
+  return size_t(a->nq > 0 ? a->nq : 1) * size_t(score_ld(a)) * sizeof(float);
+}
+
+dsa_status dsa_indexer_scores(const dsa_indexer_topk_args* a, float* scores, int64_t ld, void* stream) {
+  clear_error();
+  dsa_status st = check_indexer_args(a, false);
+  if (st != DSA_OK) return st;
+  if (a->nq == 0) return DSA_OK;
+  if (!scores || !aligned16(scores)) return fail(DSA_ERR_INVALID_ARG, "indexer_scores: scores NULL or misaligned");
+  if (ld < max_visible(a) || ld % 4 != 0) return fail(DSA_ERR_INVALID_ARG, "indexer_scores: ld too small or not % 4");
+  return launch_indexer_scores(a, scores, ld, max_visible(a), as_stream(stream));
+}
+
+dsa_status dsa_topk_from_scores(const dsa_indexer_topk_args* a, const float* scores, int64_t ld, void* stream) {
+  clear_error();
+  dsa_status st = check_indexer_args(a, true);
+  if (st != DSA_OK) return st;
+  if (a->nq == 0) return DSA_OK;
+  if (!scores || !aligned16(scores)) return fail(DSA_ERR_INVALID_ARG, "topk: scores NULL or misaligned");
+  if (ld < max_visible(a) || ld % 4 != 0) return fail(DSA_ERR_INVALID_ARG, "topk: ld too small or not % 4");
+  return launch_topk(a, scores, ld, max_visible(a), as_stream(stream));
+}
+
+dsa_status dsa_indexer_topk(const dsa_indexer_topk_args* a, void* stream) {
+  clear_error();
+  dsa_status st = check_indexer_args(a, true);
+  if (st != DSA_OK) return st;
+  if (a->nq == 0) return DSA_OK;
+  const size_t need = size_t(a->nq) * size_t(score_ld(a)) * sizeof(float);
+  if (!a->workspace || a->workspace_bytes < need || !aligned16(a->workspace))
+    return fail(DSA_ERR_WORKSPACE, "indexer_topk: workspace missing, misaligned or smaller than "
+                                       "dsa_indexer_topk_workspace()");
+  float* scores = static_cast<float*>(a->workspace);
+  st = launch_indexer_scores(a, scores, score_ld(a), max_visible(a), as_stream(stream));
+  if (st != DSA_OK) return st;
+  return launch_topk(a, scores, score_ld(a), max_visible(a), as_stream(stream));
+}
+
+dsa_status dsa_sparse_attn(const dsa_sparse_attn_args* a, void* stream) {
+  clear_error();
+  if (!a) return fail(DSA_ERR_INVALID_ARG, "sparse_attn: args is NULL");
+  if (a->nq < 0 || a->n_rows < 0 || a->k_tot < 0 || a->n_heads < 1 || a->d_qk < 1 || a->d_v < 1 ||
+      a->d_v > a->d_qk)
+    return fail(DSA_ERR_INVALID_ARG, "sparse_attn: bad sizes (need d_v <= d_qk)");
+  if (a->dtype != DSA_F32 && a->dtype != DSA_BF16) return fail(DSA_ERR_UNSUPPORTED, "sparse_attn: dtype");
+  if (a->nq == 0) return DSA_OK;
+  if (!a->q || !a->out || (a->k_tot > 0 && (!a->idx || !a->kv)))
+    return fail(DSA_ERR_INVALID_ARG, "sparse_attn: NULL pointer");
+  if (a->k_tot > 0 && a->n_rows < 1) return fail(DSA_ERR_INVALID_ARG, "sparse_attn: n_rows must be >= 1");
+  if (!aligned16(a->q) || !aligned16(a->out) || (a->kv && !aligned16(a->kv)))
+    return fail(DSA_ERR_INVALID_ARG, "sparse_attn: q / kv / out must be 16-byte aligned");
+  return launch_sparse_attn(a, as_stream(stream));
+}
+
+dsa_status dsa_rerange(const void* in, void* out, int32_t num_tokens, int64_t row_bytes, int32_t cp_size, int32_t mode,
+                       int32_t pad_to_cp, int32_t inverse, void* stream) {
+  clear_error();
+  if (num_tokens < 0 || cp_size < 1 || row_bytes < 16 || row_bytes % 16 != 0 || row_bytes / 16 > INT32_MAX)
+    return fail(DSA_ERR_INVALID_ARG, "rerange: need num_tokens >= 0, cp_size >= 1, row_bytes % 16 == 0");
+  if (!valid_mode(mode)) return fail(DSA_ERR_INVALID_ARG, "rerange: unknown split mode");
+  int32_t rows_concat = 0;
+  dsa_cp_sizes(num_tokens, cp_size, 0, mode, pad_to_cp, nullptr, nullptr, &rows_concat);
+  const int n_out = inverse ? rows_concat : num_tokens;
+  if (n_out == 0) return DSA_OK;
+  if (!in || !out) return fail(DSA_ERR_INVALID_ARG, "rerange: NULL pointer");
+  if (!aligned16(in) || !aligned16(out)) return fail(DSA_ERR_INVALID_ARG, "rerange: pointers must be 16-byte aligned");
+  const int n_in = inverse ? num_tokens : rows_concat;
+  const char* ib = static_cast<const char*>(in);
+  const char* ob = static_cast<const char*>(out);
+  if (ib < ob + int64_t(n_out) * row_bytes && ob < ib + int64_t(n_in) * row_bytes)
+    return fail(DSA_ERR_INVALID_ARG, "rerange: in and out overlap");
+  return launch_rerange(in, out, num_tokens, row_bytes, cp_size, mode, pad_to_cp, inverse, n_out, as_stream(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,74 @@
+// Internal helpers shared by the gfx950 kernels and the host entry points of libdsa.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+
+#include "dsa.h"
+
+namespace dsa {
+
+// ---------------------------------------------------------------------------------------------
+// Host-side error reporting: a per-thread message behind dsa_last_error().
+// ---------------------------------------------------------------------------------------------
+void set_error(const std::string& msg);
+void clear_error();
+dsa_status fail(dsa_status code, const std::string& msg);
+dsa_status check_launch(const char* what);
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// ---------------------------------------------------------------------------------------------
+// Device helpers
+// ---------------------------------------------------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+__device__ inline void raise_flag(int32_t* err_flag, int32_t bits) {
+  if (err_flag) atomicOr(err_flag, bits);
+}
+
+// Causal view of local query row i: request b, extent E (keys seen), key offset kv0.
+// Returns false (and flags) when the row is not covered by the local cu-seqlens.
+struct QueryView {
+  int b;
+  int E;
+  int kv0;
+};
+
+__device__ inline bool query_view(const int32_t* __restrict__ cu_q, const int32_t* __restrict__ used_kv,
+                                  const int32_t* __restrict__ cu_kv, int batch, int stride, int i,
+                                  QueryView* v) {
+  // largest b with cu_q[b] <= i, among requests that actually own rows
+  int lo = 0, hi = batch;  // invariant: cu_q[lo] <= i < cu_q[hi]
+  if (i < cu_q[0] || i >= cu_q[batch]) return false;
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (cu_q[mid] <= i) lo = mid; else hi = mid;
+  }
+  const int nb = cu_q[lo + 1] - cu_q[lo];
+  const int j = i - cu_q[lo];
+  v->b = lo;
+  v->E = used_kv[lo] - (nb - 1 - j) * stride;
+  v->kv0 = cu_kv[lo];
+  return true;
+}
+
+__device__ inline float bf16_bits_to_float(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// float -> bfloat16 bits, round to nearest even (finite inputs)
+__device__ inline uint16_t float_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+}  // namespace dsa

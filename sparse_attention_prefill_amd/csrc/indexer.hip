@@ -1,0 +1,273 @@
+// (2) Lightning-indexer scores on gfx950.
+//
+// [xLLM-CP] "feat: DeepSeek-V4 DSA context-parallel on NPU", Design, data-flow step (3) and
+// Implementation §4: the indexer's query, weights and top-k use the rank's local rows and
+// local cu-seqlens, while the index keys cover the full token stream.
+//
+//   score(i, s) = sum_h w[i,h] * max(0, q_hat[i,h,:] . k_hat[kv0(i) + s, :]),   s < Ev(i)
+//
+// Kernels:
+//  * indexer_mfma<bf16|fp8>: 64 heads x 128. A workgroup of 8 waves owns 8 consecutive local
+//    queries (one per wave, whose 64 x 128 query block stays in VGPRs as the MFMA A operand)
+//    and sweeps 64-key tiles of the union of their causal key ranges; tiles are staged in LDS
+//    with direct global->LDS loads (double buffered) and shared by the 8 waves. Each wave
+//    computes the 64 heads x 64 keys logits on 32x32 MFMAs (bf16 32x32x16, or fp8 32x32x64),
+//    then applies ReLU, the head weight and the head sum in fp32: the 32x32 accumulator layout
+//    puts one key per lane and 16 heads per lane, so the head sum is 32 in-lane FMAs plus one
+//    cross-half add. Tiles outside a wave's range are skipped by that wave.
+//    fp8: q_scale folds into the head weight and k_scale multiplies the head sum (both > 0).
+//  * indexer_generic: float32 / bf16, small shapes (VALU, one thread per (query, key)).
+#include "dsa_internal.h"
+
+namespace dsa {
+namespace {
+
+// ---------------------------------------------------------------------------------------------
+// Generic VALU kernel
+// ---------------------------------------------------------------------------------------------
+constexpr int kGenThreads = 256;
+
+template <typename T> __device__ inline float ld_elt(const T* p, int64_t i);
+template <> __device__ inline float ld_elt<float>(const float* p, int64_t i) { return p[i]; }
+template <> __device__ inline float ld_elt<uint16_t>(const uint16_t* p, int64_t i) { return bf16_bits_to_float(p[i]); }
+
+template <typename T>
+__global__ __launch_bounds__(kGenThreads) void indexer_generic(
+    const T* __restrict__ qi, const float* __restrict__ w, const T* __restrict__ ki, const int32_t* __restrict__ cu_q,
+    const int32_t* __restrict__ used_kv, const int32_t* __restrict__ cu_kv, int batch, int stride, int ratio,
+    int nq, int nk, int H, int D, int max_vis, float* __restrict__ scores, int64_t ld, int32_t* __restrict__ err_flag) {
+  extern __shared__ float sq[];  // [H*D] query block, then [H] weights
+  const int i = blockIdx.y;
+  QueryView v;
+  if (!query_view(cu_q, used_kv, cu_kv, batch, stride, i, &v)) return;
+  const int ev = ratio > 1 ? v.E / ratio : v.E;
+  if (v.E < 1 || ev > max_vis || v.kv0 < 0 || int64_t(v.kv0) + ev > nk) {
+    if (threadIdx.x == 0 && blockIdx.x == 0) raise_flag(err_flag, DSA_DEVERR_EXTENT);
+    return;
+  }
+  for (int e = threadIdx.x; e < H * D; e += kGenThreads) sq[e] = ld_elt(qi, int64_t(i) * H * D + e);
+  for (int e = threadIdx.x; e < H; e += kGenThreads) sq[H * D + e] = w[int64_t(i) * H + e];
+  __syncthreads();
+  const int s = blockIdx.x * kGenThreads + threadIdx.x;
+  if (s >= ev) return;
+  const int64_t krow = int64_t(v.kv0 + s) * D;
+  float acc = 0.f;
+  for (int h = 0; h < H; ++h) {
+    float dot = 0.f;
+    for (int d = 0; d < D; ++d) dot = fmaf(sq[h * D + d], ld_elt(ki, krow + d), dot);
+    acc = fmaf(sq[H * D + h], fmaxf(dot, 0.f), acc);
+  }
+  scores[int64_t(i) * ld + s] = acc + 0.f;  // -0.0 -> +0.0
+}
+
+// ---------------------------------------------------------------------------------------------
+// MFMA kernel: 64 heads x 128
+// ---------------------------------------------------------------------------------------------
+constexpr int kHi = 64, kDi = 128;
+constexpr int kWaves = 8, kThreads = kWaves * 64;
+constexpr int kKeyTile = 64;
+
+template <bool FP8>
+struct IdxCfg {
+  static constexpr int kKeyBytes = FP8 ? kDi : kDi * 2;          // 128 or 256
+  static constexpr int kChunks = kKeyBytes / 16;                  // 8 or 16
+  static constexpr int kTileBytes = kKeyTile * kKeyBytes;         // 8 or 16 KiB
+  static constexpr int kLoads = kKeyTile * kChunks / kThreads;    // direct loads per lane per tile: 1 or 2
+};
+
+__device__ inline int kswz(int n, int c, int chunks) { return chunks >= 8 ? (c ^ (n & 7)) : c; }
+
+template <bool FP8>
+__global__ __launch_bounds__(kThreads, 1) void indexer_mfma(
+    const unsigned char* __restrict__ qi, const float* __restrict__ q_scale, const float* __restrict__ w,
+    const unsigned char* __restrict__ ki, const float* __restrict__ k_scale, const int32_t* __restrict__ cu_q,
+    const int32_t* __restrict__ used_kv, const int32_t* __restrict__ cu_kv, int batch, int stride, int ratio, int nq,
+    int nk, int max_vis, float* __restrict__ scores, int64_t ld, int32_t* __restrict__ err_flag) {
+  using C = IdxCfg<FP8>;
+  __shared__ __attribute__((aligned(16))) unsigned char tiles[2 * C::kTileBytes];
+  __shared__ int s_lo[kWaves], s_hi[kWaves];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int i = blockIdx.x * kWaves + wave;
+
+  // this wave's query: absolute key range [lo, hi)
+  int lo = 0, hi = 0, ev = 0;
+  QueryView v{0, 0, 0};
+  bool ok = false;
+  if (i < nq && query_view(cu_q, used_kv, cu_kv, batch, stride, i, &v)) {
+    ev = ratio > 1 ? v.E / ratio : v.E;
+    ok = v.E >= 1 && ev <= max_vis && v.kv0 >= 0 && int64_t(v.kv0) + ev <= nk;
+    if (!ok && lane == 0) raise_flag(err_flag, DSA_DEVERR_EXTENT);
+    if (ok) {
+      lo = v.kv0;
+      hi = v.kv0 + ev;
+    }
+  }
+  if (!ok) lo = hi = 0;
+  if (lane == 0) {
+    s_lo[wave] = ok && hi > lo ? lo : INT32_MAX;
+    s_hi[wave] = ok && hi > lo ? hi : INT32_MIN;
+  }
+  __syncthreads();
+  int glo = INT32_MAX, ghi = INT32_MIN;
+#pragma unroll
+  for (int k = 0; k < kWaves; ++k) {
+    glo = min(glo, s_lo[k]);
+    ghi = max(ghi, s_hi[k]);
+  }
+  if (ghi <= glo) return;  // uniform: nothing to score in this workgroup
+  const int n_tiles = (ghi - glo + kKeyTile - 1) / kKeyTile;
+
+  // ---- A operand: this wave's query block, heads 32m + l32, d-slices per k-step ----
+  constexpr int kKsteps = FP8 ? kDi / 64 : kDi / 16;  // 2 or 8
+  typedef typename std::conditional<FP8, i32x8, bf16x8>::type AOp;
+  AOp qa[2][kKsteps];
+  float wv[2][16];  // weights of the 16 heads this lane holds per head block, in output layout
+  if (ok) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const unsigned char* qrow = qi + (int64_t(i) * kHi + 32 * m + l32) * (FP8 ? kDi : kDi * 2);
+#pragma unroll
+      for (int ks = 0; ks < kKsteps; ++ks) {
+        if constexpr (FP8) {
+          const i32x4* p = reinterpret_cast<const i32x4*>(qrow + 64 * ks + 32 * half);
+          const i32x4 x0 = p[0], x1 = p[1];
+          qa[m][ks] = i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        } else {
+          qa[m][ks] = *reinterpret_cast<const bf16x8*>(qrow + 2 * (16 * ks + 8 * half));
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int hh = 32 * m + 8 * (r >> 2) + 4 * half + (r & 3);
+        float wt = w[int64_t(i) * kHi + hh];
+        if constexpr (FP8) wt *= q_scale[int64_t(i) * kHi + hh];
+        wv[m][r] = wt;
+      }
+    }
+  }
+
+  // ---- staging: tile t holds keys glo + 64t + [0,64); lane loads 16-byte chunks ----
+  auto issue_tile = [&](int t, int buf) {
+    unsigned char* dst = tiles + buf * C::kTileBytes;
+#pragma unroll
+    for (int j = 0; j < C::kLoads; ++j) {
+      const int f0 = 64 * (C::kLoads * wave + j);
+      const int f = f0 + lane;
+      const int n = f / C::kChunks;
+      const int cp = f - n * C::kChunks;
+      const int c = kswz(n, cp, C::kChunks);
+      int row = glo + t * kKeyTile + n;
+      row = row < nk ? row : nk - 1;
+      const unsigned char* src = ki + int64_t(row) * C::kKeyBytes + c * 16;
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(dst + f0 * 16), 16, 0, 0);
+    }
+  };
+
+  issue_tile(0, 0);
+  for (int t = 0; t < n_tiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < n_tiles) {
+      issue_tile(t + 1, buf ^ 1);
+      if constexpr (C::kLoads == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    __syncthreads();
+    const int key0 = glo + t * kKeyTile;
+    if (ok && key0 < hi && key0 + kKeyTile > lo) {  // wave-uniform
+      const unsigned char* tb = tiles + buf * C::kTileBytes;
+      f32x16 acc[2][2];
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) acc[m][nb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < kKsteps; ++ks) {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          const int n = 32 * nb + l32;
+          if constexpr (FP8) {
+            const int c0 = 4 * ks + 2 * half;  // two 16-byte chunks: d in [64ks + 32half, +32)
+            const i32x4 x0 = *reinterpret_cast<const i32x4*>(tb + n * C::kKeyBytes + kswz(n, c0, C::kChunks) * 16);
+            const i32x4 x1 =
+                *reinterpret_cast<const i32x4*>(tb + n * C::kKeyBytes + kswz(n, c0 + 1, C::kChunks) * 16);
+            const i32x8 kb = i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+              acc[m][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[m][ks], kb, acc[m][nb], 0, 0, 0, 127,
+                                                                           0, 127);
+          } else {
+            const int c = 2 * ks + half;
+            const bf16x8 kb = *reinterpret_cast<const bf16x8*>(tb + n * C::kKeyBytes + kswz(n, c, C::kChunks) * 16);
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+              acc[m][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[m][ks], kb, acc[m][nb], 0, 0, 0);
+          }
+        }
+      }
+      // epilogue: lane holds key 32nb + l32 and heads 32m + 8(r/4) + 4half + r%4
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        float sacc = 0.f;
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sacc = fmaf(wv[m][r], fmaxf(acc[m][nb][r], 0.f), sacc);
+        sacc += __shfl_xor(sacc, 32, 64);
+        const int key = key0 + 32 * nb + l32;
+        if (half == 0 && key >= lo && key < hi) {
+          if constexpr (FP8) sacc *= k_scale[key];
+          scores[int64_t(i) * ld + (key - lo)] = sacc + 0.f;  // -0.0 -> +0.0
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+dsa_status launch_indexer_scores(const dsa_indexer_topk_args* a, float* scores, int64_t ld, int max_vis,
+                                 hipStream_t stream) {
+  if (a->nq == 0) return DSA_OK;
+  const int stride = a->q_stride, ratio = a->compress_ratio;
+  if (a->n_heads == kHi && a->head_dim == kDi && (a->dtype == DSA_BF16 || a->dtype == DSA_FP8_E4M3)) {
+    const dim3 grid((a->nq + kWaves - 1) / kWaves);
+    if (a->dtype == DSA_BF16) {
+      hipLaunchKernelGGL(indexer_mfma<false>, grid, dim3(kThreads), 0, stream,
+                         static_cast<const unsigned char*>(a->q_idx), a->q_scale, a->weights,
+                         static_cast<const unsigned char*>(a->k_idx), a->k_scale, a->cu_seqlens_q, a->seqused_kv,
+                         a->cu_seqlens_kv, a->batch, stride, ratio, a->nq, a->nk, max_vis, scores, ld, a->err_flag);
+    } else {
+      hipLaunchKernelGGL(indexer_mfma<true>, grid, dim3(kThreads), 0, stream,
+                         static_cast<const unsigned char*>(a->q_idx), a->q_scale, a->weights,
+                         static_cast<const unsigned char*>(a->k_idx), a->k_scale, a->cu_seqlens_q, a->seqused_kv,
+                         a->cu_seqlens_kv, a->batch, stride, ratio, a->nq, a->nk, max_vis, scores, ld, a->err_flag);
+    }
+    return check_launch("indexer_mfma");
+  }
+  if (a->dtype == DSA_FP8_E4M3) return fail(DSA_ERR_UNSUPPORTED, "indexer: fp8 needs 64 heads x 128");
+  if (a->n_heads * a->head_dim > 8192 || a->n_heads > 256)
+    return fail(DSA_ERR_UNSUPPORTED, "indexer: shape not supported by the generic kernel");
+  const dim3 grid((max_vis + kGenThreads - 1) / kGenThreads, a->nq);
+  const size_t lds = sizeof(float) * (size_t(a->n_heads) * a->head_dim + a->n_heads);
+  if (a->dtype == DSA_F32) {
+    hipLaunchKernelGGL(indexer_generic<float>, grid, dim3(kGenThreads), lds, stream,
+                       static_cast<const float*>(a->q_idx), a->weights, static_cast<const float*>(a->k_idx),
+                       a->cu_seqlens_q, a->seqused_kv, a->cu_seqlens_kv, a->batch, stride, ratio, a->nq, a->nk,
+                       a->n_heads, a->head_dim, max_vis, scores, ld, a->err_flag);
+  } else if (a->dtype == DSA_BF16) {
+    hipLaunchKernelGGL(indexer_generic<uint16_t>, grid, dim3(kGenThreads), lds, stream,
+                       static_cast<const uint16_t*>(a->q_idx), a->weights, static_cast<const uint16_t*>(a->k_idx),
+                       a->cu_seqlens_q, a->seqused_kv, a->cu_seqlens_kv, a->batch, stride, ratio, a->nq, a->nk,
+                       a->n_heads, a->head_dim, max_vis, scores, ld, a->err_flag);
+  } else {
+    return fail(DSA_ERR_UNSUPPORTED, "indexer: unknown dtype");
+  }
+  return check_launch("indexer_generic");
+}
+
+}  // namespace dsa

@@ -204,39 +204,43 @@ def stream_inputs(wl: Workload, variant="normal"):
 def query_inputs(wl: Workload, tokens, variant="normal"):
     """Per-query tensors for the given global token ids (pads: id < 0 give zero rows).
 
-    Returns q [n,H,D_qk], q_idx [n,H_i,D_i], w [n,H_i] float32, and q_scale [n,H_i] for fp8.
+    Returns q [n,H,D_qk], q_idx [n,H_i,D_i], w [n,H_i] float32, and q_scale [n,H_i] for fp8,
+    filled token by token straight into the storage dtype.
     """
     tokens = np.asarray(tokens, dtype=np.int64)
     n = len(tokens)
     unit = variant == "unit"
-    q = np.zeros((n, wl.H, wl.Dqk))
-    qi = np.zeros((n, wl.Hi, wl.Di))
-    w = np.zeros((n, wl.Hi))
-    qs = np.ones((n, wl.Hi))
     sq = 1.0 if unit else 1.0 / np.sqrt(wl.Dqk)
     si = 1.0 if unit else 1.0 / np.sqrt(wl.Di)
+    q = np.zeros((n, wl.H, wl.Dqk), dtype=np.float32 if wl.attn_dtype == "f32" else np.uint16)
+    fp8 = wl.idx_dtype == "fp8"
+    qi = np.zeros((n, wl.Hi, wl.Di), dtype={"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}[wl.idx_dtype])
+    w = np.zeros((n, wl.Hi), dtype=np.float32)
+    qs = np.ones((n, wl.Hi), dtype=np.float32)
     for j, t in enumerate(tokens):
         if t < 0:
             continue
         g = _rng(wl.wid, T_Q, t, variant)
-        q[j] = g.standard_normal((wl.H, wl.Dqk)) * sq
+        q[j] = _store(g.standard_normal((wl.H, wl.Dqk)) * sq, wl.attn_dtype)
         g = _rng(wl.wid, T_QIDX, t, variant)
         if variant == "int":
-            qi[j] = g.integers(-4, 5, size=(wl.Hi, wl.Di))
+            x = g.integers(-4, 5, size=(wl.Hi, wl.Di)).astype(np.float64)
             w[j] = g.integers(-2, 3, size=wl.Hi)
-            qs[j] = np.ldexp(1.0, -g.integers(0, 4, size=wl.Hi))
+            if fp8:
+                qs[j] = np.ldexp(1.0, -g.integers(0, 4, size=wl.Hi))
         else:
-            qi[j] = g.standard_normal((wl.Hi, wl.Di)) * si
+            x = g.standard_normal((wl.Hi, wl.Di)) * si
             w[j] = g.standard_normal(wl.Hi) / np.sqrt(wl.Hi)
-    out = {"q": _store(q, wl.attn_dtype), "w": w.astype(np.float32)}
-    if wl.idx_dtype == "fp8":
-        if variant == "int":
-            out["q_idx"] = f64_to_e4m3fn_bytes(qi)
-            out["q_scale"] = qs.astype(np.float32)
+        if fp8:
+            if variant == "int":
+                qi[j] = f64_to_e4m3fn_bytes(x)
+            else:
+                qi[j], qs[j] = _quant_fp8_rows(x)
         else:
-            out["q_idx"], out["q_scale"] = _quant_fp8_rows(qi)
-    else:
-        out["q_idx"] = _store(qi, wl.idx_dtype)
+            qi[j] = _store(x, wl.idx_dtype)
+    out = {"q": q, "w": w, "q_idx": qi}
+    if fp8:
+        out["q_scale"] = qs
     return out
 
 

@@ -1,0 +1,81 @@
+"""The C-ABI library: it loads on a machine without a GPU, exports every symbol the header
+declares, and its host-side checks reject bad arguments before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_hot_path_calls():
+    names = declared_functions()
+    for f in ("dsa_build_cp_metadata", "dsa_indexer_topk", "dsa_sparse_attn", "dsa_rerange"):
+        assert f in names
+
+
+def test_library_exports_every_declared_symbol():
+    import sparse_attention_prefill_amd as D
+    L = D.lib()
+    missing = [n for n in declared_functions() if not hasattr(L, n)]
+    assert not missing, missing
+
+
+def test_host_sizes():
+    import sparse_attention_prefill_amd as D
+    assert D.cp_sizes(8000, 8, 7, 0, False) == (1000, 1000, 8000)
+    assert D.cp_sizes(43013, 8, 3, 1, False) == (5377, 5377, 43013)
+    assert D.cp_sizes(11, 3, 2, 0, True) == (4, 3, 12)
+    assert D.cp_sizes(11, 3, 2, 1, False) == (4, 3, 11)
+    with pytest.raises(D.DsaError):
+        D.cp_sizes(10, 4, 4, 0, False)
+
+
+def test_host_checks_reject_before_launch():
+    import sparse_attention_prefill_amd as D
+    L = D.lib()
+    # rerange: row bytes not a multiple of 16, bad mode, rank-less sizes
+    assert L.dsa_rerange(None, None, 10, 24, 2, 0, 0, 0, None) == 1
+    assert L.dsa_rerange(None, None, 10, 32, 2, 7, 0, 0, None) == 1
+    assert L.dsa_rerange(None, None, 0, 32, 2, 1, 0, 0, None) == 0          # nothing to do
+    assert L.dsa_rerange(ctypes.c_void_p(16), ctypes.c_void_p(32), 10, 32, 2, 1, 0, 0, None) == 1  # overlap
+    assert b"overlap" in L.dsa_last_error()
+    # metadata: rank out of range
+    assert L.dsa_build_cp_metadata(None, None, 1, 8, 2, 2, 0, 0, None, None, None, None, None, None, None) == 1
+    # attention: NULL args, bad dtype
+    assert L.dsa_sparse_attn(None, None) == 1
+    a = D.binding.AttnArgs()
+    a.nq, a.n_rows, a.n_heads, a.d_qk, a.d_v, a.k_tot, a.dtype = 2, 4, 128, 576, 512, 8, 2
+    assert L.dsa_sparse_attn(ctypes.byref(a), None) == 2
+    a.dtype = 1
+    assert L.dsa_sparse_attn(ctypes.byref(a), None) == 1                      # NULL pointers
+    # indexer: top-k < 1, fp8 without scales
+    g = D.binding.IndexerArgs()
+    g.nq, g.nk, g.n_heads, g.head_dim, g.batch, g.topk, g.q_stride, g.compress_ratio = 4, 8, 64, 128, 1, 0, 1, 1
+    assert L.dsa_indexer_topk(ctypes.byref(g), None) == 1
+    g.topk, g.dtype = 16, 2
+    g.q_idx = g.weights = g.k_idx = g.cu_seqlens_q = g.seqused_kv = g.cu_seqlens_kv = g.topk_idx = 256
+    assert L.dsa_indexer_topk(ctypes.byref(g), None) == 1
+    assert b"scale" in L.dsa_last_error()
+    g.q_scale = g.k_scale = 256
+    g.max_seqlen_kv = 8
+    assert L.dsa_indexer_topk(ctypes.byref(g), None) == 3                     # no workspace
+    assert L.dsa_indexer_topk_workspace(ctypes.byref(g)) == 4 * 64 * 4
+    g.max_seqlen_kv = 200000
+    assert L.dsa_indexer_topk(ctypes.byref(g), None) == 2                     # rows too long
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    import sparse_attention_prefill_amd.binding as B
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "library_path", "/nonexistent/libdsa.so")
+    with pytest.raises(B.DsaError):
+        B.lib()

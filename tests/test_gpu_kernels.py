@@ -1,0 +1,222 @@
+"""GPU parity of each kernel in isolation, on inputs the oracle also sees.
+
+  top-k (3):     same fp32 score rows -> identical ascending id lists (bit-exact)
+  indexer (2):   same stored q/k/w -> scores within fp32 rounding; exact on integer inputs
+  attention (4): same index sets -> outputs within the attention tolerance
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synthetic as S
+from dsa_testlib import gpu, to_dev, to_f64, assert_attn_close
+
+pytestmark = pytest.mark.gpu
+
+
+def _meta_dev(lens, cp, rank, mode, dev):
+    qsl = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    m = O.cp_metadata(qsl, lens, cp, rank, mode, False)
+    d = {k: to_dev(m[k], "i32", dev) for k in ("local_query_start_loc", "local_seq_lens", "local_kv_start_loc")}
+    return m, d
+
+
+def _run_topk(scores, m, d, K, dev, ratio=1, window=0, win_start=None, kv_row_base=0):
+    import sparse_attention_prefill_amd as D
+    nq = m["n_local_real"]
+    ld = scores.shape[1]
+    max_kv = int(m["local_seq_lens"].max())
+    dummy_q = torch.zeros(nq, 1, 8, dtype=torch.float32, device=dev)
+    dummy_k = torch.zeros(1, 8, dtype=torch.float32, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    out = D.topk_from_scores(dummy_q, dummy_q[:, :, 0], dummy_k, d["local_query_start_loc"], d["local_seq_lens"],
+                             d["local_kv_start_loc"], max_kv, to_dev(scores, "f32", dev), topk=K,
+                             q_stride=m["stride"], compress_ratio=ratio, window=window,
+                             window_kv_start=win_start, kv_row_base=kv_row_base, err_flag=err)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("kind", ["normal", "ties", "zeros", "const"])
+@pytest.mark.parametrize("lens,cp,rank,K", [
+    ([700], 1, 0, 64),              # E = 1..700, short rows take everything
+    ([3000], 1, 0, 2048),           # E crosses K; 4-per-thread register path
+    ([9000], 8, 7, 2048),           # 8192 < E <= 9000: 16-per-thread path
+    ([30000], 200, 199, 2048),      # E ~ 30000: 32-per-thread path
+    ([40000], 4000, 3999, 2048),    # E ~ 40000: streamed path
+    ([131072], 16384, 16383, 2048), # E ~ 131072: streamed path, longest rows
+    ([50, 1, 300], 3, 1, 7),        # several requests, round-robin below
+])
+def test_topk_bit_exact(kind, lens, cp, rank, K):
+    dev = gpu()
+    for mode in (O.IN_SEQ, O.ROUND_ROBIN):
+        m, d = _meta_dev(lens, cp, rank, mode, dev)
+        views = O.query_views(m)
+        if not views:
+            continue
+        ld = (max(E for _, E, _ in views) + 3) // 4 * 4
+        scores = S.score_rows(len(lens) * 1000 + K, len(views), ld, kind)
+        got = _run_topk(scores, m, d, K, dev)
+        for i, (b, E, kv0) in enumerate(views):
+            want = kv0 + O.topk_positions(scores[i, :E], K)
+            row = got[i]
+            assert np.array_equal(row[:len(want)], want), (kind, i, E)
+            assert np.all(row[len(want):] == -1)
+
+
+def test_topk_compressed_and_window():
+    """x4-compressed keys (Ev = floor(E/4)) plus the 128-token window, round-robin, padded rank."""
+    dev = gpu()
+    lens = [700, 9, 3, 1300]
+    qsl = np.concatenate([[0], np.cumsum(lens)])
+    T = int(qsl[-1])
+    m, d = _meta_dev(lens, 4, 1, O.ROUND_ROBIN, dev)
+    ccs = np.concatenate([[0], np.cumsum([l // 4 for l in lens])]).astype(np.int32)
+    d["local_kv_start_loc"] = to_dev(ccs, "i32", dev)
+    views = O.query_views(m)
+    ld = (max(E // 4 for _, E, _ in views) + 4) // 4 * 4
+    scores = S.score_rows(77, len(views), ld, "ties")
+    K = 64
+    got = _run_topk(scores, m, d, K, dev, ratio=4, window=128, win_start=to_dev(qsl, "i32", dev), kv_row_base=T)
+    for i, (b, E, _) in enumerate(views):
+        want = T + ccs[b] + O.topk_positions(scores[i, :E // 4], K)
+        assert np.array_equal(got[i, :len(want)], want) and np.all(got[i, len(want):K] == -1), i
+        win = qsl[b] + O.window_positions(E, 128)
+        assert np.array_equal(got[i, K:K + len(win)], win) and np.all(got[i, K + len(win):] == -1), i
+
+
+def _indexer_case(wl, variant, dev, rows_cap=None):
+    import sparse_attention_prefill_amd as D
+    m = O.cp_metadata(wl.qsl, wl.lens, wl.cp, wl.rank, wl.mode, wl.pad)
+    toks = m["token_map"][m["token_map"] >= 0]
+    inp = S.stream_inputs(wl, variant)
+    qin = S.query_inputs(wl, toks, variant)
+    kind = {"f32": "f32", "bf16": "bf16", "fp8": "fp8"}[wl.idx_dtype]
+    cu_kv = inp["kv_cmp_start"] if wl.compress > 1 else m["local_kv_start_loc"]
+    max_kv = int(m["local_seq_lens"].max())
+    ev_max = max_kv // wl.compress if wl.compress > 1 else max_kv
+    ld = (ev_max + 63) // 64 * 64
+    nq = len(toks)
+    scores = torch.full((nq, ld), float("nan"), dtype=torch.float32, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    D.indexer_scores(to_dev(qin["q_idx"], kind, dev), to_dev(qin["w"], "f32", dev), to_dev(inp["k_idx"], kind, dev),
+                     to_dev(m["local_query_start_loc"], "i32", dev), to_dev(m["local_seq_lens"], "i32", dev),
+                     to_dev(cu_kv, "i32", dev), max_kv, scores, q_stride=m["stride"], compress_ratio=wl.compress,
+                     q_scale=to_dev(qin["q_scale"], "f32", dev) if "q_scale" in qin else None,
+                     k_scale=to_dev(inp["k_scale"], "f32", dev) if "k_scale" in inp else None, err_flag=err)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    got = scores.cpu().numpy()
+    k_hat = O.dequant_k(inp["k_idx"], inp.get("k_scale"), wl.idx_dtype)
+    views = O.query_views(m)
+    rows = range(nq) if rows_cap is None else np.unique(np.linspace(0, nq - 1, rows_cap).astype(int))
+    for i in rows:
+        b, E, kv0 = views[i]
+        q_hat = O.dequant_q(qin["q_idx"][i], qin["q_scale"][i] if "q_scale" in qin else None, wl.idx_dtype)
+        if wl.compress > 1:
+            ev = E // wl.compress
+            ref = O.indexer_scores_row(q_hat, qin["w"][i], k_hat[cu_kv[b]:cu_kv[b] + ev])
+        else:
+            ev = E
+            ref = O.indexer_scores_row(q_hat, qin["w"][i], k_hat[kv0:kv0 + E])
+        g = got[i, :ev].astype(np.float64)
+        if variant == "int":
+            assert np.array_equal(g, ref), (wl.name, i)
+            assert not np.any(np.signbit(g[g == 0])), "negative zero score"
+        else:
+            tol = 2e-5 * max(np.abs(ref).max(), 1e-30)
+            assert np.abs(g - ref).max() <= tol, (wl.name, i, np.abs(g - ref).max(), tol)
+
+
+@pytest.mark.parametrize("variant", ["normal", "int"])
+@pytest.mark.parametrize("name,kw", [
+    ("tiny_fp32_cp1", {}),
+    ("inseq_cp8_last_8k", {"lens": (3000,)}),
+    ("rr_cp8_r3_batch4", {"lens": (1500, 700, 130, 5)}),
+    ("long_131k_fp8", {"lens": (3000,)}),
+    ("rr_cp4_r1_var8_cmp4", {"lens": (1100, 1900, 13, 640)}),
+])
+def test_indexer_scores(name, kw, variant):
+    dev = gpu()
+    _indexer_case(S.WORKLOADS[name].with_(**kw), variant, dev)
+
+
+def _rand_idx(g, nq, k_tot, n_rows, frac_missing=0.1, empty_rows=()):
+    idx = g.integers(0, n_rows, size=(nq, k_tot)).astype(np.int32)
+    idx[g.random((nq, k_tot)) < frac_missing] = -1
+    for r in empty_rows:
+        idx[r] = -1
+    return idx
+
+
+@pytest.mark.parametrize("variant", ["normal", "unit"])
+@pytest.mark.parametrize("name,nq,k_tot,n_rows", [
+    ("tiny_fp32_cp1", 37, 64, 512),
+    ("tiny_fp32_cp1", 5, 100, 300),
+    ("inseq_cp8_last_8k", 24, 2048, 8192),
+    ("inseq_cp8_last_8k", 9, 2176, 5000),
+    ("inseq_cp8_last_8k", 7, 100, 130),
+    ("inseq_cp8_last_8k", 4, 1, 3),
+])
+def test_attention_on_given_sets(name, nq, k_tot, n_rows, variant):
+    dev = gpu()
+    import sparse_attention_prefill_amd as D
+    wl = S.WORKLOADS[name].with_(lens=(n_rows,))
+    inp = S.stream_inputs(wl, variant)
+    qin = S.query_inputs(wl, np.arange(nq) * 7 % n_rows, variant)
+    g = np.random.default_rng(nq * 1000 + k_tot)
+    idx = _rand_idx(g, nq, k_tot, n_rows, empty_rows=(nq - 1,) if nq > 2 else ())
+    scale = 1.0 / np.sqrt(wl.Dqk)
+    kind = wl.attn_dtype
+    lse = torch.empty(nq, wl.H, dtype=torch.float32, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    out = D.sparse_attn(to_dev(qin["q"], kind, dev), to_dev(inp["kv"], kind, dev), to_dev(idx, "i32", dev),
+                        to_dev(inp["sink"], "f32", dev), scale, wl.Dv, lse=lse, err_flag=err)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    kv = O.decode(inp["kv"], kind)
+    sink = inp["sink"].astype(np.float64)
+    ref = np.zeros((nq, wl.H, wl.Dv))
+    ref_lse = np.zeros((nq, wl.H))
+    for i in range(nq):
+        sel = idx[i][idx[i] >= 0]
+        ref[i], ref_lse[i] = O.sparse_attention_row(O.decode(qin["q"][i], kind), kv[sel], sink, scale, wl.Dv)
+    assert_attn_close(to_f64(out), ref, kind, f"{name} {variant}")
+    assert np.abs(lse.cpu().numpy() - ref_lse).max() < (1e-4 if kind == "f32" else 2e-3)
+
+
+def test_attention_every_key_is_dense_causal():
+    """Index sets = all positions 0..t: the sparse kernel reproduces dense causal attention."""
+    dev = gpu()
+    import sparse_attention_prefill_amd as D
+    T = 70
+    wl = S.WORKLOADS["inseq_cp8_last_8k"].with_(lens=(T,))
+    inp = S.stream_inputs(wl, "unit")
+    qin = S.query_inputs(wl, np.arange(T), "unit")
+    idx = np.full((T, 2048), -1, dtype=np.int32)
+    for t in range(T):
+        idx[t, :t + 1] = np.arange(t + 1)[::-1]
+    scale = 1.0 / np.sqrt(576)
+    out = D.sparse_attn(to_dev(qin["q"], "bf16", dev), to_dev(inp["kv"], "bf16", dev), to_dev(idx, "i32", dev),
+                        to_dev(inp["sink"], "f32", dev), scale, 512)
+    torch.cuda.synchronize()
+    dense = O.dense_causal_attention(O.decode_bf16(qin["q"]), O.decode_bf16(inp["kv"]),
+                                     inp["sink"].astype(np.float64), scale, 512)
+    assert_attn_close(to_f64(out), dense, "bf16", "dense causal")
+
+
+def test_attention_flags_bad_rows():
+    dev = gpu()
+    import sparse_attention_prefill_amd as D
+    wl = S.WORKLOADS["inseq_cp8_last_8k"].with_(lens=(64,))
+    inp = S.stream_inputs(wl)
+    qin = S.query_inputs(wl, np.arange(2))
+    idx = np.zeros((2, 64), dtype=np.int32)
+    idx[0, 3] = 64  # one past the end
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    D.sparse_attn(to_dev(qin["q"], "bf16", dev), to_dev(inp["kv"], "bf16", dev), to_dev(idx, "i32", dev),
+                  to_dev(inp["sink"], "f32", dev), 0.05, 512, err_flag=err)
+    torch.cuda.synchronize()
+    assert err.item() & 0x40

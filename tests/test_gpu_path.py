@@ -1,0 +1,163 @@
+"""End-to-end GPU parity of one rank's hot path: metadata -> indexer + top-k -> sparse attention.
+
+Each workload runs through the C ABI in the order and launch configuration the benchmark uses.
+The oracle checks: metadata bit-exact; top-k sets bit-exact on integer-valued inputs and within
+the tie band on Gaussian inputs; attention within tolerance on every row whose set matches.
+Full-size workloads are checked on sampled rows; reduced ones on every row.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synthetic as S
+from dsa_testlib import gpu, to_dev, to_f64, assert_attn_close, check_topk_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_rank_path(wl, variant, dev, rank=None, keep_scores=False):
+    """Run the rank's share through the library. Returns host copies of everything."""
+    import sparse_attention_prefill_amd as D
+    rank = wl.rank if rank is None else rank
+    mode = 0 if wl.mode == O.IN_SEQ else 1
+    inp = S.stream_inputs(wl, variant)
+    qsl_d = to_dev(wl.qsl, "i32", dev)
+    lens_d = to_dev(np.asarray(wl.lens), "i32", dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    meta = D.build_cp_metadata(qsl_d, lens_d, wl.T, wl.cp, rank, mode, wl.pad, err_flag=err)
+    torch.cuda.synchronize()
+    tpr, n_real, _ = D.cp_sizes(wl.T, wl.cp, rank, mode, wl.pad)
+    toks = meta["token_map"].cpu().numpy()[:n_real]
+    qin = S.query_inputs(wl, toks, variant)
+    ik = wl.idx_dtype
+    max_kv = max(wl.lens)
+    cu_kv = to_dev(inp["kv_cmp_start"], "i32", dev) if wl.compress > 1 else meta["local_kv_start_loc"]
+    q_idx = to_dev(qin["q_idx"], ik, dev)
+    kw = dict(topk=wl.topk, q_stride=int(meta["scalars"][4].item()), compress_ratio=wl.compress,
+              kv_row_base=wl.T if wl.compress > 1 else 0, window=wl.window,
+              window_kv_start=meta["local_kv_start_loc"] if wl.window else None,
+              q_scale=to_dev(qin["q_scale"], "f32", dev) if "q_scale" in qin else None,
+              k_scale=to_dev(inp["k_scale"], "f32", dev) if "k_scale" in inp else None, err_flag=err)
+    w_d = to_dev(qin["w"], "f32", dev)
+    k_d = to_dev(inp["k_idx"], ik, dev)
+    nbytes = D.indexer_topk_workspace(q_idx, w_d, k_d, meta["local_query_start_loc"], meta["local_seq_lens"], cu_kv,
+                                      max_kv, **kw)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    idx = D.indexer_topk(q_idx, w_d, k_d, meta["local_query_start_loc"], meta["local_seq_lens"], cu_kv, max_kv,
+                         workspace=ws, **kw)
+    out = D.sparse_attn(to_dev(qin["q"], wl.attn_dtype, dev), to_dev(inp["kv"], wl.attn_dtype, dev), idx,
+                        to_dev(inp["sink"], "f32", dev), 1.0 / np.sqrt(wl.Dqk), wl.Dv, err_flag=err)
+    torch.cuda.synchronize()
+    res = dict(meta={k: (v.cpu().numpy() if v is not None else None) for k, v in meta.items()}, err=err.item(),
+               idx=idx.cpu().numpy(), out=out, toks=toks, inp=inp, qin=qin, n_real=n_real, tpr=tpr)
+    if keep_scores:
+        ld = nbytes // 4 // max(n_real, 1)
+        res["scores"] = ws.view(torch.float32)[:n_real * ld].view(n_real, ld).cpu().numpy()
+    return res
+
+
+def check_against_oracle(wl, variant, res, rows=None, min_same=0.99):
+    m = O.cp_metadata(wl.qsl, wl.lens, wl.cp, wl.rank, wl.mode, wl.pad)
+    assert res["err"] == 0
+    for k in ("local_query_start_loc", "local_seq_lens", "local_kv_start_loc", "token_map"):
+        assert np.array_equal(res["meta"][k], m[k]), k
+    n = m["n_local_real"]
+    rows = list(range(n)) if rows is None else list(rows)
+    ora = O.run_path(m, {**res["inp"], **{k: v for k, v in res["qin"].items()}}, wl, rows=rows, want_scores=True)
+    K = wl.topk
+    views = O.query_views(m)
+    base = [((wl.T + res["inp"]["kv_cmp_start"][views[i][0]]) if wl.compress > 1 else views[i][2]) for i in rows]
+    gpu_topk = [res["idx"][i, :K] for i in rows]
+    if variant == "int":
+        for n_, i in enumerate(rows):
+            g = gpu_topk[n_][gpu_topk[n_] >= 0]
+            assert np.array_equal(g, ora["topk_ids"][n_]), f"row {i}: integer-valued top-k differs"
+        same = len(rows)
+    else:
+        same = check_topk_rows(gpu_topk, ora["topk_ids"], ora["scores"], K, base, rows=rows)
+    assert same >= min_same * len(rows), f"only {same}/{len(rows)} rows with identical sets"
+    if wl.window:
+        for n_, i in enumerate(rows):
+            w = res["idx"][i, K:]
+            assert np.array_equal(w[w >= 0], ora["window_ids"][n_]), f"row {i}: window rows"
+    got = to_f64(res["out"])
+    keep = [n_ for n_, i in enumerate(rows)
+            if np.array_equal(np.sort(gpu_topk[n_][gpu_topk[n_] >= 0]), ora["topk_ids"][n_])]
+    assert_attn_close(got[[rows[k] for k in keep]], ora["out"][keep], wl.attn_dtype, wl.name)
+    return ora
+
+
+REDUCED = [
+    ("tiny_fp32_cp1", {}),
+    ("inseq_cp8_last_8k", {"lens": (4096,)}),
+    ("rr_cp8_r3_batch4", {"lens": (4400, 2600, 800, 5)}),
+    ("long_131k_fp8", {"lens": (4096,)}),
+    ("rr_cp4_r1_var8_cmp4", {"lens": (3000, 9001, 700, 1234)}),
+]
+
+
+@pytest.mark.parametrize("name,kw", REDUCED)
+def test_path_reduced_every_row(name, kw):
+    dev = gpu()
+    wl = S.WORKLOADS[name].with_(**kw)
+    res = gpu_rank_path(wl, "normal", dev)
+    n = res["n_real"]
+    rows = range(n) if n <= 200 else np.unique(np.linspace(0, n - 1, 200).astype(int))
+    check_against_oracle(wl, "normal", res, rows=rows)
+
+
+@pytest.mark.parametrize("name,kw", REDUCED)
+def test_path_integer_inputs_topk_exact(name, kw):
+    dev = gpu()
+    wl = S.WORKLOADS[name].with_(**kw)
+    res = gpu_rank_path(wl, "int", dev)
+    n = res["n_real"]
+    rows = range(n) if n <= 120 else np.unique(np.linspace(0, n - 1, 120).astype(int))
+    check_against_oracle(wl, "int", res, rows=rows)
+
+
+@pytest.mark.parametrize("name", ["inseq_cp8_last_8k", "rr_cp8_r3_batch4", "rr_cp4_r1_var8_cmp4", "long_131k_fp8"])
+def test_path_full_size_sampled(name):
+    dev = gpu()
+    wl = S.WORKLOADS[name]
+    res = gpu_rank_path(wl, "normal", dev, keep_scores=True)
+    n = res["n_real"]
+    rows = np.unique(np.concatenate([[0, 1, n - 2, n - 1], np.linspace(0, n - 1, 10).astype(int)]))
+    ora = check_against_oracle(wl, "normal", res, rows=rows, min_same=0.75)
+    for n_, i in enumerate(rows):  # the score rows themselves
+        ref = ora["scores"][n_]
+        g = res["scores"][i, :len(ref)].astype(np.float64)
+        assert np.abs(g - ref).max() <= 2e-5 * max(np.abs(ref).max(), 1e-30), (name, i)
+
+
+@pytest.mark.parametrize("name,kw", [("rr_cp8_r3_batch4", {"lens": (2100, 900, 300, 5), "topk": 256}),
+                                     ("rr_cp4_r1_var8_cmp4", {"lens": (1500, 2222, 77, 901), "topk": 256}),
+                                     ("inseq_cp8_last_8k", {"lens": (1000, 3001), "topk": 512})])
+def test_all_ranks_reranged_equal_cp1_bitwise(name, kw):
+    """Every rank's share run in turn, concatenated by rank and reranged == the cp = 1 run."""
+    dev = gpu()
+    import sparse_attention_prefill_amd as D
+    wl = S.WORKLOADS[name].with_(**kw)
+    mode = 0 if wl.mode == O.IN_SEQ else 1
+    full = gpu_rank_path(wl.with_(cp=1, rank=0), "normal", dev)["out"]
+    parts = []
+    for r in range(wl.cp):
+        res = gpu_rank_path(wl, "normal", dev, rank=r)
+        rows = res["tpr"] if wl.pad else res["n_real"]
+        part = torch.zeros(rows, wl.H, wl.Dv, dtype=res["out"].dtype, device=dev)
+        part[:res["n_real"]] = res["out"]
+        parts.append(part)
+    concat = torch.cat(parts)
+    back = D.rerange(concat.view(concat.shape[0], -1), wl.T, wl.cp, mode, wl.pad).view(wl.T, wl.H, wl.Dv)
+    torch.cuda.synchronize()
+    assert torch.equal(back.view(torch.int16), full.view(torch.int16))
+
+
+def test_path_is_deterministic():
+    dev = gpu()
+    wl = S.WORKLOADS["rr_cp8_r3_batch4"].with_(lens=(3000, 1000, 17))
+    a = gpu_rank_path(wl, "normal", dev)
+    b = gpu_rank_path(wl, "normal", dev)
+    assert np.array_equal(a["idx"], b["idx"])
+    assert torch.equal(a["out"].view(torch.int16), b["out"].view(torch.int16))
