@@ -37,6 +37,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU time budget of the oracle sample")
     p.add_argument("--profile-only", action="store_true", help="no CPU baseline, fewer prints (for rocprofv3)")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="only run a plain copy of MIB MiB (the rerange kernel in its identity mode) three times; "
+                        "its FETCH_SIZE / WRITE_SIZE counters scale the HBM traffic of the other kernels")
     return p.parse_args()
 
 
@@ -59,6 +62,15 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20)
+        src = torch.ones(n // 1152, 576, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            D.rerange(src, src.shape[0], 1, 0, False, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": src.numel() * 2, "launches": 3}))
+        return
     wl = S.WORKLOADS[args.workload]
     mode = 0 if wl.mode == "in_seq" else 1
 

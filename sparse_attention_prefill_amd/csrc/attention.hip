@@ -15,8 +15,10 @@
 //    wave then runs S^T = K Q^T (32 rows x 32 heads, Q^T held in VGPRs) and O += P V on
 //    32x32x16 bf16 MFMAs. S^T puts one head per lane, so the softmax reductions are in-lane,
 //    and its accumulator layout is directly the A operand of P V (the contraction order over
-//    rows is permuted identically on both operands). Online softmax starts from the sink
-//    (m = sink, l = 1) and rescales O only when a head's running max grows by more than 2^8.
+//    rows is permuted identically on both operands). The softmax reference max m of each head is
+//    fixed from the first tile (and the sink), so O is never rescaled: every later probability is
+//    e^(l - m) <= 2^64, far inside fp32 / bf16 range. If a later logit ever exceeds m by more
+//    than that, the workgroup reruns the query once with m = the exact max seen in the first run.
 //  * sparse_attn_generic: float32 or bf16, small head counts (n_heads * d_v <= 4096); VALU.
 #include "dsa_internal.h"
 
@@ -143,18 +145,30 @@ __global__ __launch_bounds__(kGenThreads) void sparse_attn_generic(
 // ---------------------------------------------------------------------------------------------
 constexpr int kH = 128, kDqk = 576, kDv = 512;
 constexpr int kWaves = 4, kThreads = kWaves * 64;
-constexpr int kTile = 64;                       // KV rows per LDS tile
-constexpr int kRowBytes = kDqk * 2;             // 1152
-constexpr int kChunks = kRowBytes / 16;         // 72 x 16-byte chunks per row
-constexpr int kTileBytes = kTile * kRowBytes;   // 73728
-constexpr int kMaxKtot = 2304;                  // selected rows per query held in LDS (<= 9 KiB)
-constexpr int kLoadsPerWave = kTile * kChunks / (kWaves * 64);  // 18
-constexpr float kRescaleThresh = 8.f;           // log2 units
+constexpr int kTile = 64;                          // KV rows per LDS tile
+constexpr int kRowBytes = kDqk * 2;                // 1152 bytes per KV row in HBM
+constexpr int kLatBytes = kDv * 2;                 // 1024: latent columns of a row in LDS
+constexpr int kRopeBytes = kRowBytes - kLatBytes;  // 128: rope columns
+constexpr int kLatTile = kTile * kLatBytes;        // 64 KiB
+constexpr int kTileBytes = kLatTile + kTile * kRopeBytes;  // 72 KiB
+constexpr int kMaxKtot = 2304;                     // selected rows per query held in LDS (9 KiB)
+constexpr int kLoadsPerWave = 18;                  // 16 latent rows + 2 rope instructions
+constexpr float kOverflowMargin = 64.f;            // log2 units: e^(l - m) stays <= 2^64
 
-static_assert(kTile * kChunks % (kWaves * 64) == 0, "tile must split evenly into wave loads");
+// LDS tile layout: latent region [64 rows][64 chunks of 16 B], then rope region [64 rows][8
+// chunks]; chunk c of row n sits at physical chunk c ^ (n & 7) (XOR swizzle inside groups of 8),
+// so the 32 rows read by one MFMA operand load, and the 8 rows of one transposed V read, spread
+// over all LDS banks.
+__device__ inline int lat_off(int n, int c) { return n * kLatBytes + ((c ^ (n & 7)) << 4); }
+__device__ inline int rope_off(int n, int c) { return kLatTile + n * kRopeBytes + ((c ^ (n & 7)) << 4); }
 
-// physical 16-byte chunk of logical chunk c in tile row n (XOR swizzle inside groups of 8)
-__device__ inline int swz(int n, int c) { return c ^ (n & 7); }
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16: inside each 16-lane group, lane o receives element o%4 of the 4-element
+// runs addressed by lanes 4j + o/4 (j = 0..3) -- a 16x4 -> 4x16 transpose.
+__device__ inline s16x4 lds_read_tr16(const unsigned char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+}
 
 __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
@@ -163,7 +177,8 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   unsigned char* tiles = lds;                                        // 2 x kTileBytes
   int* rows = reinterpret_cast<int*>(lds + 2 * kTileBytes);          // [kMaxKtot] compacted row ids
-  int* scan = rows + kMaxKtot;                                       // [kWaves + 1]
+  int* scan = rows + kMaxKtot;                                       // [kWaves + 1], then the rerun flag
+  int* redo_flag = scan + kWaves + 1;
 
   const int i = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -172,7 +187,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
 
   // ---- selected row ids -> LDS, validated and compacted (order kept) ----
   {
-    constexpr int kPer = kMaxKtot / kThreads;  // 16 entries per thread
+    constexpr int kPer = kMaxKtot / kThreads;  // 9 entries per thread
     int vals[kPer];
     int cnt = 0;
     bool bad = false;
@@ -208,6 +223,11 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
     for (int k = 0; k < kPer; ++k)
       if (vals[k] >= 0) rows[pos++] = vals[k];
     __syncthreads();
+    // pad the tail of the last tile with row 0 (a valid row; masked out of the softmax)
+    const int n_sel0 = scan[kWaves];
+    const int padded = (n_sel0 + kTile - 1) / kTile * kTile;
+    for (int e = n_sel0 + tid; e < padded; e += kThreads) rows[e] = 0;
+    __syncthreads();
   }
   const int n_sel = scan[kWaves];
   const int n_tiles = (n_sel + kTile - 1) / kTile;
@@ -220,116 +240,147 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
     for (int ks = 0; ks < kDqk / 16; ++ks) qreg[ks] = qp[2 * ks];
   }
 
-  // ---- gather of one tile: lane takes 16-byte chunks f = 64*(18*wave + j) + lane ----
+  // ---- gather of one tile into LDS with direct global->LDS loads ----
+  //  latent: instruction j of this wave moves row n = 16*wave + j (one uniform row id, 64 lanes x
+  //          16 B = 1024 B; lane l lands in physical chunk l, i.e. logical chunk l ^ (n & 7));
+  //  rope:   2 instructions of 8 rows x 8 chunks (lane l: row 8r + l/8, physical chunk l%8).
+  const unsigned char* kvb = reinterpret_cast<const unsigned char*>(kv);
   auto issue_tile = [&](int t, int buf) {
+    int lane16 = lane << 4;
+    asm volatile("" : "+v"(lane16));  // keep per-lane offsets out of loop-invariant hoisting
     unsigned char* dst = tiles + buf * kTileBytes;
+    const int my_row = rows[t * kTile + 16 * wave + (lane & 15)];  // this wave's 16 latent rows
 #pragma unroll
-    for (int j = 0; j < kLoadsPerWave; ++j) {
-      const int f0 = 64 * (kLoadsPerWave * wave + j);
-      const int f = f0 + lane;
-      const int n = f / kChunks;
-      const int cp = f - n * kChunks;  // physical chunk in the LDS row
-      const int c = swz(n, cp);        // logical chunk it holds
-      const int e = t * kTile + n;
-      const int r = e < n_sel ? rows[e] : 0;
-      const unsigned char* src = reinterpret_cast<const unsigned char*>(kv) + int64_t(r) * kRowBytes + c * 16;
-      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(dst + f0 * 16), 16, 0, 0);
+    for (int j = 0; j < 16; ++j) {
+      const int r = __builtin_amdgcn_readlane(my_row, j);
+      const unsigned char* src = kvb + int64_t(r) * kRowBytes + (lane16 ^ ((j & 7) << 4));
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(dst + (16 * wave + j) * kLatBytes),
+                                       16, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n0 = 16 * wave + 8 * j;  // rows n0 + lane/8; n & 7 == lane/8
+      const int r = rows[t * kTile + n0 + (lane >> 3)];
+      const int c = (lane & 7) ^ (lane >> 3);
+      const unsigned char* src = kvb + int64_t(r) * kRowBytes + kLatBytes + (c << 4);
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(dst + kLatTile + n0 * kRopeBytes),
+                                       16, 0, 0);
     }
   };
 
-  // ---- running softmax state (one head per lane; both halves agree) ----
-  float m_run = sink ? sink[h] * kLog2e : -INFINITY;
-  float l_run = sink ? 1.f : 0.f;
+  // per-lane LDS byte offsets (tile-relative):
+  //  K operand rows n = 32hb + l32, logical chunk 2ks + half -> k_off[ks % 4] + 128*(ks / 4)
+  //  rope operand chunk 2(ks-32) + half -> r_off[ks - 32]
+  //  transposed V reads (see lds_read_tr16): lane L supplies row 4*(L/32) + (L%16)/4 of a
+  //  16-row slab, columns 32db + 16((L/16)&1) + 4(L%4): chunk 4(db ^ half) + (v_cl ^ (L%16)/4)
+  int k_off[4], r_off[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    k_off[m] = l32 * kLatBytes + (((2 * m + half) ^ (l32 & 7)) << 4);
+    r_off[m] = kLatTile + l32 * kRopeBytes + (((2 * m + half) ^ (l32 & 7)) << 4);
+  }
+  const int v_n = 4 * half + ((lane & 15) >> 2);
+  const int v_cl = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int v_lane = v_n * kLatBytes + ((v_cl ^ (v_n & 3)) << 4) + ((lane & 1) << 3);
+  const int v_even = v_lane + 64 * half, v_odd = v_lane - 64 * half;  // + 64*db for db even / odd
+
+  const float sink_l2 = sink ? sink[h] * kLog2e : -INFINITY;
   f32x16 oacc[kDv / 32];
-#pragma unroll
-  for (int db = 0; db < kDv / 32; ++db) oacc[db] = f32x16{};
+  float m_used = -INFINITY, l_run = 0.f, m_seen = -INFINITY;
+  if (tid == 0) *redo_flag = 0;
 
-  if (n_tiles > 0) issue_tile(0, 0);
-
-  for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < n_tiles) {
-      issue_tile(t + 1, buf ^ 1);
-      asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
-    __syncthreads();
-    const unsigned char* tb = tiles + buf * kTileBytes;
-
-    // S^T[n][h] for n in [0,64): two 32-row blocks
-    f32x16 s0 = f32x16{}, s1 = f32x16{};
+#pragma unroll 1
+  for (int attempt = 0; attempt < 2; ++attempt) {
+    // attempt 0: m from the first tile; attempt 1 (rare): m = exact max of every logit seen
+    // (an empty selection keeps m = sink, l = 1: out = 0, lse = sink)
+    m_used = attempt == 0 ? sink_l2 : fmaxf(sink_l2, m_seen);
+    l_run = sink ? exp2f(sink_l2 - m_used) : 0.f;
 #pragma unroll
-    for (int ks = 0; ks < kDqk / 16; ++ks) {
-      const int c = 2 * ks + half;
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(tb + l32 * kRowBytes + swz(l32, c) * 16);
-      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(tb + (32 + l32) * kRowBytes + swz(32 + l32, c) * 16);
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[ks], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[ks], s1, 0, 0, 0);
-    }
+    for (int db = 0; db < kDv / 32; ++db) oacc[db] = f32x16{};
+    bool overflow = false;
 
-    // mask rows past n_sel; lane holds rows n = 32nb + 8(v/4) + 4half + v%4
-    const int valid = n_sel - t * kTile;  // rows of this tile that are real (>= 1)
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int n0 = 8 * (v >> 2) + 4 * half + (v & 3);
-      s0[v] = n0 < valid ? s0[v] * scale_log2 : -INFINITY;
-      s1[v] = n0 + 32 < valid ? s1[v] * scale_log2 : -INFINITY;
-      tmax = fmaxf(tmax, fmaxf(s0[v], s1[v]));
-    }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-
-    // lazy rescale: only when some head's max grew by more than 2^8 (or was -inf)
-    const bool grow = tmax > m_run + kRescaleThresh || (m_run == -INFINITY && tmax > -INFINITY);
-    if (__any(grow)) {
-      const float m_new = fmaxf(m_run, tmax);
-      const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);
-      l_run *= alpha;
-      m_run = m_new;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float av = __shfl(alpha, 8 * (v >> 2) + 4 * half + (v & 3), 64);
-#pragma unroll
-        for (int db = 0; db < kDv / 32; ++db) oacc[db][v] *= av;
+    if (n_tiles > 0) issue_tile(0, 0);
+    for (int t = 0; t < n_tiles; ++t) {
+      const int buf = t & 1;
+      if (t + 1 < n_tiles) {
+        issue_tile(t + 1, buf ^ 1);
+        asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       }
-    }
+      __syncthreads();
+      const unsigned char* tb = tiles + buf * kTileBytes;
+      const int valid = n_sel - t * kTile;  // real rows in this tile (>= 1)
 
-    // probabilities (bf16) in the PV A-operand layout; row sums
-    float psum = 0.f;
-    bf16x8 pa[4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+      for (int hb = 0; hb < 2; ++hb) {  // 32-row halves of the tile
+        // S^T[n][h] = K[n,:] . Q[h,:] for rows n = 32hb + 0..31
+        f32x16 s = f32x16{};
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int v = 8 * (kk & 1) + j;
-        const float sv = (kk < 2) ? s0[v] : s1[v];
-        const float p = m_run == -INFINITY ? 0.f : exp2f(sv - m_run);
-        psum += p;
-        pa[kk][j] = (__bf16)p;
-      }
-    }
-    psum += __shfl_xor(psum, 32, 64);
-    l_run += psum;
-
-    // O[h][d] += P[h][n] V[n][d]; row of k-slot j in step kk: n = 16kk + 8(j/4) + 4half + j%4
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-#pragma unroll
-      for (int db = 0; db < kDv / 32; ++db) {
-        const int d = 32 * db + l32;
-        bf16x8 vb;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int n = 16 * kk + 8 * (j >> 2) + 4 * half + (j & 3);
-          const uint16_t bits =
-              *reinterpret_cast<const uint16_t*>(tb + n * kRowBytes + swz(n, d >> 3) * 16 + (d & 7) * 2);
-          vb[j] = __builtin_bit_cast(__bf16, bits);
+        for (int ks = 0; ks < kDv / 16; ++ks) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(tb + k_off[ks & 3] + 128 * (ks >> 2) + 32 * hb * kLatBytes);
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], s, 0, 0, 0);
         }
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[kk], vb, oacc[db], 0, 0, 0);
+#pragma unroll
+        for (int ks = kDv / 16; ks < kDqk / 16; ++ks) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(tb + r_off[ks - kDv / 16] + 32 * hb * kRopeBytes);
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], s, 0, 0, 0);
+        }
+
+        // lane holds rows n = 32hb + 8(v/4) + 4half + v%4 of head h; mask rows past the selection
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int n = 32 * hb + 8 * (v >> 2) + 4 * half + (v & 3);
+          s[v] = n < valid ? s[v] * scale_log2 : -INFINITY;
+          tmax = fmaxf(tmax, s[v]);
+        }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        m_seen = fmaxf(m_seen, tmax);
+        if (attempt == 0 && t == 0 && hb == 0) {
+          // O is still zero: fix the reference max here, no rescale needed
+          m_used = fmaxf(sink_l2, tmax);
+          l_run = sink ? exp2f(sink_l2 - m_used) : 0.f;
+        }
+        overflow |= tmax > m_used + kOverflowMargin;
+
+        // probabilities (bf16) in the P.V A-operand layout; row sums
+        float psum = 0.f;
+        bf16x8 pa[2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) {
+            const float p = exp2f(s[8 * kk + jj] - m_used);
+            psum += p;
+            pa[kk][jj] = (__bf16)p;
+          }
+        }
+        psum += __shfl_xor(psum, 32, 64);
+        l_run += psum;
+
+        // O[h][d] += P[h][n] V[n][d]; k-slot jj of step kk is row 32hb + 16kk + 8(jj/4) + 4half + jj%4
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const unsigned char* vb = tb + (32 * hb + 16 * kk) * kLatBytes;
+#pragma unroll
+          for (int db = 0; db < kDv / 32; ++db) {
+            const unsigned char* p0 = vb + ((db & 1) ? v_odd : v_even) + 64 * db;
+            const s16x4 lo = lds_read_tr16(p0);
+            const s16x4 hi = lds_read_tr16(p0 + 8 * kLatBytes);
+            const s16x8 vv = s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[kk], __builtin_bit_cast(bf16x8, vv), oacc[db],
+                                                                0, 0, 0);
+          }
+        }
       }
+      __syncthreads();  // every wave is done with this buffer before it is refilled
     }
-    __syncthreads();  // every wave is done with this buffer before it is refilled
+    if (attempt == 0) {
+      if (__any(overflow) && lane == 0) atomicOr(redo_flag, 1);
+      __syncthreads();
+      if (*redo_flag == 0) break;  // uniform
+    }
   }
 
   // ---- normalise and store: lane holds d = 32db + l32 for heads 8(v/4) + 4half + v%4 ----
@@ -342,12 +393,12 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
 #pragma unroll
     for (int db = 0; db < kDv / 32; ++db) op[hl * kDv + 32 * db + l32] = float_to_bf16_bits(oacc[db][v] * iv);
   }
-  if (lse && half == 0) lse[int64_t(i) * kH + h] = l_run > 0.f ? (m_run + log2f(l_run)) / kLog2e : -INFINITY;
+  if (lse && half == 0) lse[int64_t(i) * kH + h] = l_run > 0.f ? (m_used + log2f(l_run)) / kLog2e : -INFINITY;
 }
 
 }  // namespace
 
-size_t mla_attn_lds_bytes() { return 2 * kTileBytes + (kMaxKtot + kWaves + 1) * sizeof(int); }
+size_t mla_attn_lds_bytes() { return 2 * kTileBytes + (kMaxKtot + kWaves + 2) * sizeof(int); }
 
 dsa_status launch_sparse_attn(const dsa_sparse_attn_args* a, hipStream_t stream) {
   if (a->nq == 0) return DSA_OK;

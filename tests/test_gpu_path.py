@@ -75,7 +75,8 @@ def check_against_oracle(wl, variant, res, rows=None, min_same=0.99):
             assert np.array_equal(g, ora["topk_ids"][n_]), f"row {i}: integer-valued top-k differs"
         same = len(rows)
     else:
-        same = check_topk_rows(gpu_topk, ora["topk_ids"], ora["scores"], K, base, rows=rows)
+        same = check_topk_rows(gpu_topk, ora["topk_ids"], ora["scores"], K, base, rows=rows,
+                               delta_rel=1e-4 if wl.idx_dtype == "fp8" else 1e-5)
     assert same >= min_same * len(rows), f"only {same}/{len(rows)} rows with identical sets"
     if wl.window:
         for n_, i in enumerate(rows):
@@ -128,7 +129,9 @@ def test_path_full_size_sampled(name):
     for n_, i in enumerate(rows):  # the score rows themselves
         ref = ora["scores"][n_]
         g = res["scores"][i, :len(ref)].astype(np.float64)
-        assert np.abs(g - ref).max() <= 2e-5 * max(np.abs(ref).max(), 1e-30), (name, i)
+        if len(ref):
+            tol = (1e-4 if wl.idx_dtype == "fp8" else 2e-5) * max(np.abs(ref).max(), 1e-30)
+            assert np.abs(g - ref).max() <= tol, (name, i)
 
 
 @pytest.mark.parametrize("name,kw", [("rr_cp8_r3_batch4", {"lens": (2100, 900, 300, 5), "topk": 256}),
