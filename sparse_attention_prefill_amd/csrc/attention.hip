@@ -153,14 +153,21 @@ constexpr int kLatTile = kTile * kLatBytes;        // 64 KiB
 constexpr int kTileBytes = kLatTile + kTile * kRopeBytes;  // 72 KiB
 constexpr int kMaxKtot = 2304;                     // selected rows per query held in LDS (9 KiB)
 constexpr int kLoadsPerWave = 18;                  // 16 latent rows + 2 rope instructions
+constexpr int kLookK = 2, kLookV = 1;             // LDS operand reads issued ahead of their MFMA
 constexpr float kOverflowMargin = 64.f;            // log2 units: e^(l - m) stays <= 2^64
 
 // LDS tile layout: latent region [64 rows][64 chunks of 16 B], then rope region [64 rows][8
-// chunks]; chunk c of row n sits at physical chunk c ^ (n & 7) (XOR swizzle inside groups of 8),
-// so the 32 rows read by one MFMA operand load, and the 8 rows of one transposed V read, spread
-// over all LDS banks.
-__device__ inline int lat_off(int n, int c) { return n * kLatBytes + ((c ^ (n & 7)) << 4); }
-__device__ inline int rope_off(int n, int c) { return kLatTile + n * kRopeBytes + ((c ^ (n & 7)) << 4); }
+// chunks]. Chunk c of latent row n sits at physical chunk c ^ lat_swz(n), of rope row n at
+// c ^ rope_swz(n). lat_swz permutes the 16-chunk groups so that (a) the 16 rows of one K operand
+// read (same logical chunk) hit 16 distinct 16-byte bank groups and (b) each transposed V read
+// (4 consecutive rows x 32 contiguous bytes per 16-lane group, 4 rows x 64 bytes per 32 lanes)
+// touches distinct banks; both hold for 32 or 64 four-byte banks. rope_swz does (a) for 128-byte
+// rows.
+__device__ inline int lat_swz(int n) {
+  const int j = n & 3, b = (n >> 2) & 1, a = (n >> 3) & 1;
+  return ((((j >> 1) ^ a) << 3) | ((j & 1) << 2) | ((j >> 1) << 1) | b);
+}
+__device__ inline int rope_swz(int n) { return ((n >> 1) & 3) | (((n ^ (n >> 3)) & 1) << 2); }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
@@ -242,7 +249,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
 
   // ---- gather of one tile into LDS with direct global->LDS loads ----
   //  latent: instruction j of this wave moves row n = 16*wave + j (one uniform row id, 64 lanes x
-  //          16 B = 1024 B; lane l lands in physical chunk l, i.e. logical chunk l ^ (n & 7));
+  //          16 B = 1024 B; lane l lands in physical chunk l, i.e. logical chunk l ^ lat_swz(n));
   //  rope:   2 instructions of 8 rows x 8 chunks (lane l: row 8r + l/8, physical chunk l%8).
   const unsigned char* kvb = reinterpret_cast<const unsigned char*>(kv);
   auto issue_tile = [&](int t, int buf) {
@@ -253,36 +260,42 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int r = __builtin_amdgcn_readlane(my_row, j);
-      const unsigned char* src = kvb + int64_t(r) * kRowBytes + (lane16 ^ ((j & 7) << 4));
+      const unsigned char* src = kvb + int64_t(r) * kRowBytes + (lane16 ^ (lat_swz(j) << 4));  // (16w+j)&15 == j
       __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(dst + (16 * wave + j) * kLatBytes),
                                        16, 0, 0);
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int n0 = 16 * wave + 8 * j;  // rows n0 + lane/8; n & 7 == lane/8
+      const int n0 = 16 * wave + 8 * j;  // rows n0 + lane/8
       const int r = rows[t * kTile + n0 + (lane >> 3)];
-      const int c = (lane & 7) ^ (lane >> 3);
+      const int c = (lane & 7) ^ rope_swz(n0 + (lane >> 3));
       const unsigned char* src = kvb + int64_t(r) * kRowBytes + kLatBytes + (c << 4);
       __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(dst + kLatTile + n0 * kRopeBytes),
                                        16, 0, 0);
     }
   };
 
-  // per-lane LDS byte offsets (tile-relative):
-  //  K operand rows n = 32hb + l32, logical chunk 2ks + half -> k_off[ks % 4] + 128*(ks / 4)
-  //  rope operand chunk 2(ks-32) + half -> r_off[ks - 32]
-  //  transposed V reads (see lds_read_tr16): lane L supplies row 4*(L/32) + (L%16)/4 of a
-  //  16-row slab, columns 32db + 16((L/16)&1) + 4(L%4): chunk 4(db ^ half) + (v_cl ^ (L%16)/4)
-  int k_off[4], r_off[4];
+  // per-lane LDS byte offsets (tile-relative). A swizzled chunk offset is (c << 4) ^ (f << 4); the
+  // XOR with the per-lane part is done per read (one VALU op) instead of holding every variant:
+  //  K operand (rows n = 32hb + l32, logical chunk 2ks + half):
+  //      k_base + ((32 ks) ^ k_x) + 32hb*1024      [k_x = (half ^ lat_swz(l32)) << 4]
+  //  rope operand (logical chunk 2(ks-32) + half): r_base + ((32 (ks-32)) ^ r_x) + 32hb*128
+  //  transposed V reads (see lds_read_tr16): lane L supplies row v_n = 4*(L/32) + (L%16)/4 of an
+  //  8-row slab (lo: rows 16kk + v_n, hi: 16kk + 8 + v_n) and columns 32db + 16((L/16)&1) +
+  //  4(L%4) .. +3 (logical chunk 4db + v_cl): v_base[hl] + ((64 db) ^ v_x[hl])
+  const int k_base = l32 * kLatBytes, k_x0 = (half ^ lat_swz(l32)) << 4;
+  const int r_base = kLatTile + l32 * kRopeBytes, r_x0 = (half ^ rope_swz(l32)) << 4;
+  int v_base[2], v_x0[2];
+  {
+    const int v_n = 4 * half + ((lane & 15) >> 2);
+    const int v_cl = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    k_off[m] = l32 * kLatBytes + (((2 * m + half) ^ (l32 & 7)) << 4);
-    r_off[m] = kLatTile + l32 * kRopeBytes + (((2 * m + half) ^ (l32 & 7)) << 4);
+    for (int hl = 0; hl < 2; ++hl) {
+      const int n = v_n + 8 * hl;
+      v_base[hl] = n * kLatBytes + ((lane & 1) << 3);
+      v_x0[hl] = (v_cl ^ lat_swz(n)) << 4;
+    }
   }
-  const int v_n = 4 * half + ((lane & 15) >> 2);
-  const int v_cl = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-  const int v_lane = v_n * kLatBytes + ((v_cl ^ (v_n & 3)) << 4) + ((lane & 1) << 3);
-  const int v_even = v_lane + 64 * half, v_odd = v_lane - 64 * half;  // + 64*db for db even / odd
 
   const float sink_l2 = sink ? sink[h] * kLog2e : -INFINITY;
   f32x16 oacc[kDv / 32];
@@ -316,25 +329,41 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
       for (int hb = 0; hb < 2; ++hb) {  // 32-row halves of the tile
         // S^T[n][h] = K[n,:] . Q[h,:] for rows n = 32hb + 0..31
         f32x16 s = f32x16{};
+        {
+          int k_x = k_x0, r_x = r_x0;
+          asm volatile("" : "+v"(k_x), "+v"(r_x));  // recomputed per half-tile: no hoisting of 36 offsets
+          bf16x8 a[kDqk / 16];
 #pragma unroll
-        for (int ks = 0; ks < kDv / 16; ++ks) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(tb + k_off[ks & 3] + 128 * (ks >> 2) + 32 * hb * kLatBytes);
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], s, 0, 0, 0);
-        }
+          for (int ks = 0; ks < kDv / 16; ++ks)
+            a[ks] = *reinterpret_cast<const bf16x8*>(tb + k_base + ((32 * ks) ^ k_x) + 32 * hb * kLatBytes);
 #pragma unroll
-        for (int ks = kDv / 16; ks < kDqk / 16; ++ks) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(tb + r_off[ks - kDv / 16] + 32 * hb * kRopeBytes);
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], s, 0, 0, 0);
+          for (int ks = kDv / 16; ks < kDqk / 16; ++ks)
+            a[ks] = *reinterpret_cast<const bf16x8*>(tb + r_base + ((32 * (ks - kDv / 16)) ^ r_x) + 32 * hb * kRopeBytes);
+#pragma unroll
+          for (int ks = 0; ks < kDqk / 16; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], qreg[ks], s, 0, 0, 0);
+          // issue order: kLookK operand reads ahead, then one MFMA per read
+          __builtin_amdgcn_sched_group_barrier(0x100, kLookK, 0);
+#pragma unroll
+          for (int ks = 0; ks < kDqk / 16 - kLookK; ++ks) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, kLookK, 0);
         }
 
         // lane holds rows n = 32hb + 8(v/4) + 4half + v%4 of head h; mask rows past the selection
+        // (only the last tile can be partial: wave-uniform branch)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s[v] *= scale_log2;
+        if (valid < kTile) {
+          const int lim = valid - 32 * hb - 4 * half;
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            if (8 * (v >> 2) + (v & 3) >= lim) s[v] = -INFINITY;
+        }
         float tmax = -INFINITY;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int n = 32 * hb + 8 * (v >> 2) + 4 * half + (v & 3);
-          s[v] = n < valid ? s[v] * scale_log2 : -INFINITY;
-          tmax = fmaxf(tmax, s[v]);
-        }
+        for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, s[v]);
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
         m_seen = fmaxf(m_seen, tmax);
         if (attempt == 0 && t == 0 && hb == 0) {
@@ -351,7 +380,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
         for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
           for (int jj = 0; jj < 8; ++jj) {
-            const float p = exp2f(s[8 * kk + jj] - m_used);
+            const float p = __builtin_amdgcn_exp2f(s[8 * kk + jj] - m_used);  // v_exp_f32; tiny -> 0
             psum += p;
             pa[kk][jj] = (__bf16)p;
           }
@@ -363,15 +392,27 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
           const unsigned char* vb = tb + (32 * hb + 16 * kk) * kLatBytes;
+          int vx0 = v_x0[0], vx1 = v_x0[1];
+          asm volatile("" : "+v"(vx0), "+v"(vx1));
+          s16x4 lo[kDv / 32], hi[kDv / 32];
 #pragma unroll
           for (int db = 0; db < kDv / 32; ++db) {
-            const unsigned char* p0 = vb + ((db & 1) ? v_odd : v_even) + 64 * db;
-            const s16x4 lo = lds_read_tr16(p0);
-            const s16x4 hi = lds_read_tr16(p0 + 8 * kLatBytes);
-            const s16x8 vv = s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            lo[db] = lds_read_tr16(vb + v_base[0] + ((64 * db) ^ vx0));
+            hi[db] = lds_read_tr16(vb + v_base[1] + ((64 * db) ^ vx1));
+          }
+#pragma unroll
+          for (int db = 0; db < kDv / 32; ++db) {
+            const s16x8 vv = s16x8{lo[db][0], lo[db][1], lo[db][2], lo[db][3], hi[db][0], hi[db][1], hi[db][2], hi[db][3]};
             oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[kk], __builtin_bit_cast(bf16x8, vv), oacc[db],
                                                                 0, 0, 0);
           }
+          __builtin_amdgcn_sched_group_barrier(0x100, 2 * kLookV, 0);
+#pragma unroll
+          for (int db = 0; db < kDv / 32 - kLookV; ++db) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, kLookV, 0);
         }
       }
       __syncthreads();  // every wave is done with this buffer before it is refilled
