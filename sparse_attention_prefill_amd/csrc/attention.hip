@@ -188,7 +188,8 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
   int* redo_flag = scan + kWaves + 1;
 
   const int i = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave (known to the compiler)
   const int half = lane >> 5, l32 = lane & 31;
   const int h = wave * 32 + l32;  // this lane's head in S^T / softmax
 
@@ -255,23 +256,20 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
   auto issue_tile = [&](int t, int buf) {
     int lane16 = lane << 4;
     asm volatile("" : "+v"(lane16));  // keep per-lane offsets out of loop-invariant hoisting
-    unsigned char* dst = tiles + buf * kTileBytes;
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_offset(tiles + buf * kTileBytes));
     const int my_row = rows[t * kTile + 16 * wave + (lane & 15)];  // this wave's 16 latent rows
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int r = __builtin_amdgcn_readlane(my_row, j);
-      const unsigned char* src = kvb + int64_t(r) * kRowBytes + (lane16 ^ (lat_swz(j) << 4));  // (16w+j)&15 == j
-      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(dst + (16 * wave + j) * kLatBytes),
-                                       16, 0, 0);
+      lds_dma16_s(kvb + int64_t(r) * kRowBytes, uint32_t(lane16 ^ (lat_swz(j) << 4)),  // (16w+j)&15 == j
+                  dst + uint32_t((16 * wave + j) * kLatBytes));
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int n0 = 16 * wave + 8 * j;  // rows n0 + lane/8
       const int r = rows[t * kTile + n0 + (lane >> 3)];
       const int c = (lane & 7) ^ rope_swz(n0 + (lane >> 3));
-      const unsigned char* src = kvb + int64_t(r) * kRowBytes + kLatBytes + (c << 4);
-      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(dst + kLatTile + n0 * kRopeBytes),
-                                       16, 0, 0);
+      lds_dma16_v(kvb + int64_t(r) * kRowBytes + kLatBytes + (c << 4), dst + uint32_t(kLatTile + n0 * kRopeBytes));
     }
   };
 
@@ -317,11 +315,10 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
       const int buf = t & 1;
       if (t + 1 < n_tiles) {
         issue_tile(t + 1, buf ^ 1);
-        asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+        DSA_TILE_BARRIER_VMCNT(18);  // this tile landed; the next one (18 loads) stays in flight
       } else {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        DSA_TILE_BARRIER_VMCNT(0);
       }
-      __syncthreads();
       const unsigned char* tb = tiles + buf * kTileBytes;
       const int valid = n_sel - t * kTile;  // real rows in this tile (>= 1)
 
@@ -415,7 +412,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
           __builtin_amdgcn_sched_group_barrier(0x008, kLookV, 0);
         }
       }
-      __syncthreads();  // every wave is done with this buffer before it is refilled
+      DSA_TILE_BARRIER_LDS();  // every wave is done with this buffer before it is refilled
     }
     if (attempt == 0) {
       if (__any(overflow) && lane == 0) atomicOr(redo_flag, 1);

@@ -32,6 +32,34 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
+// Workgroup barrier for double-buffered direct global->LDS tile loads. __syncthreads() carries a
+// workgroup memory fence that waits for EVERY outstanding vector-memory load (vmcnt(0)),
+// including the next tile's prefetch, which would serialise load and compute. These barriers
+// wait only for this wave's loads of the current tile (the newest `n` loads may stay in flight)
+// and for its LDS reads; the memory clobber keeps the compiler from moving accesses across.
+#define DSA_TILE_BARRIER_VMCNT(n) asm volatile("s_waitcnt vmcnt(" #n ")\n\ts_barrier" ::: "memory")
+#define DSA_TILE_BARRIER_LDS() asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
+
+// Direct global->LDS 16-byte loads: lane l's 16 bytes land at lds_base + 16*l (lds_base is
+// wave-uniform, passed in M0). Issued as inline asm so the compiler does not add its own
+// conservative vmcnt waits before later LDS reads; the caller owns the bookkeeping through
+// DSA_TILE_BARRIER_VMCNT. M0 is written only here.
+__device__ inline uint32_t lds_offset(const void* p) {
+  return uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p));
+}
+// uniform 64-bit global base + per-lane 32-bit byte offset
+__device__ inline void lds_dma16_s(const void* gbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gbase),
+               "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory", "m0");
+}
+// per-lane 64-bit global address
+__device__ inline void lds_dma16_v(const void* gaddr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gaddr),
+               "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory", "m0");
+}
+
 __device__ inline void raise_flag(int32_t* err_flag, int32_t bits) {
   if (err_flag) atomicOr(err_flag, bits);
 }

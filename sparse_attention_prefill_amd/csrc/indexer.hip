@@ -87,7 +87,8 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_mfma(
   __shared__ __attribute__((aligned(16))) unsigned char tiles[2 * C::kTileBytes];
   __shared__ int s_lo[kWaves], s_hi[kWaves];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave (known to the compiler)
   const int half = lane >> 5, l32 = lane & 31;
   const int i = blockIdx.x * kWaves + wave;
 
@@ -161,7 +162,7 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_mfma(
       int row = glo + t * kKeyTile + n;
       row = row < nk ? row : nk - 1;
       const unsigned char* src = ki + int64_t(row) * C::kKeyBytes + c * 16;
-      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(dst + f0 * 16), 16, 0, 0);
+      lds_dma16_v(src, __builtin_amdgcn_readfirstlane(lds_offset(dst + f0 * 16)));
     }
   };
 
@@ -170,12 +171,11 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_mfma(
     const int buf = t & 1;
     if (t + 1 < n_tiles) {
       issue_tile(t + 1, buf ^ 1);
-      if constexpr (C::kLoads == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
+      if constexpr (C::kLoads == 2) DSA_TILE_BARRIER_VMCNT(2);
+      else DSA_TILE_BARRIER_VMCNT(1);
     } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      DSA_TILE_BARRIER_VMCNT(0);
     }
-    __syncthreads();
     const int key0 = glo + t * kKeyTile;
     if (ok && key0 < hi && key0 + kKeyTile > lo) {  // wave-uniform
       const unsigned char* tb = tiles + buf * C::kTileBytes;
@@ -224,7 +224,7 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_mfma(
         }
       }
     }
-    __syncthreads();
+    DSA_TILE_BARRIER_LDS();
   }
 }
 
