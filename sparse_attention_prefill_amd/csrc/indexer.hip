@@ -9,7 +9,8 @@
 // Kernels:
 //  * indexer_mfma<bf16|fp8>: 64 heads x 128. A workgroup of 8 waves owns 8 consecutive local
 //    queries (one per wave, whose 64 x 128 query block stays in VGPRs as the MFMA A operand)
-//    and sweeps 64-key tiles of the union of their causal key ranges; tiles are staged in LDS
+//    and sweeps 128-key tiles of one 2048-key chunk (grid.y) of the union of their causal key
+//    ranges, so even short query batches fill the GPU; tiles are staged in LDS
 //    with direct global->LDS loads (double buffered) and shared by the 8 waves. Each wave
 //    computes the 64 heads x 64 keys logits on 32x32 MFMAs (bf16 32x32x16, or fp8 32x32x64),
 //    then applies ReLU, the head weight and the head sum in fp32: the 32x32 accumulator layout
@@ -65,17 +66,26 @@ __global__ __launch_bounds__(kGenThreads) void indexer_generic(
 // ---------------------------------------------------------------------------------------------
 constexpr int kHi = 64, kDi = 128;
 constexpr int kWaves = 8, kThreads = kWaves * 64;
-constexpr int kKeyTile = 64;
+constexpr int kKeyTile = 128;
+constexpr int kChunkKeys = 16 * kKeyTile;  // keys per workgroup (grid.y splits longer ranges)
 
 template <bool FP8>
 struct IdxCfg {
   static constexpr int kKeyBytes = FP8 ? kDi : kDi * 2;          // 128 or 256
   static constexpr int kChunks = kKeyBytes / 16;                  // 8 or 16
   static constexpr int kTileBytes = kKeyTile * kKeyBytes;         // 8 or 16 KiB
-  static constexpr int kLoads = kKeyTile * kChunks / kThreads;    // direct loads per lane per tile: 1 or 2
+  static constexpr int kLoads = kKeyTile * kChunks / kThreads;    // direct loads per lane per tile: 2 or 4
 };
 
-__device__ inline int kswz(int n, int c, int chunks) { return chunks >= 8 ? (c ^ (n & 7)) : c; }
+// Physical 16-byte chunk of logical chunk c of key row n in an LDS tile. 256-byte rows (bf16):
+// XOR with n & 15, so the 16 rows read together by one MFMA operand load hit 16 distinct bank
+// groups. 128-byte rows (fp8): a 3-bit XOR chosen so that rows n and n + 8 (which share banks)
+// also differ.
+template <int CHUNKS>
+__device__ inline int kswz(int n, int c) {
+  if constexpr (CHUNKS == 16) return c ^ (n & 15);
+  else return c ^ (((n >> 1) & 3) | (((n ^ (n >> 3)) & 1) << 2));
+}
 
 template <bool FP8>
 __global__ __launch_bounds__(kThreads, 1) void indexer_mfma(
@@ -106,6 +116,7 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_mfma(
     }
   }
   if (!ok) lo = hi = 0;
+  const int q_origin = lo;  // score column 0 of this query
   if (lane == 0) {
     s_lo[wave] = ok && hi > lo ? lo : INT32_MAX;
     s_hi[wave] = ok && hi > lo ? hi : INT32_MIN;
@@ -117,7 +128,12 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_mfma(
     glo = min(glo, s_lo[k]);
     ghi = max(ghi, s_hi[k]);
   }
+  // this workgroup's slice of the union key range: chunk blockIdx.y
+  glo = glo + int(blockIdx.y) * kChunkKeys;
+  ghi = min(ghi, glo + kChunkKeys);
   if (ghi <= glo) return;  // uniform: nothing to score in this workgroup
+  lo = max(lo, glo);
+  hi = min(hi, ghi);
   const int n_tiles = (ghi - glo + kKeyTile - 1) / kKeyTile;
 
   // ---- A operand: this wave's query block, heads 32m + l32, d-slices per k-step ----
@@ -158,7 +174,7 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_mfma(
       const int f = f0 + lane;
       const int n = f / C::kChunks;
       const int cp = f - n * C::kChunks;
-      const int c = kswz(n, cp, C::kChunks);
+      const int c = kswz<C::kChunks>(n, cp);
       int row = glo + t * kKeyTile + n;
       row = row < nk ? row : nk - 1;
       const unsigned char* src = ki + int64_t(row) * C::kKeyBytes + c * 16;
@@ -171,56 +187,48 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_mfma(
     const int buf = t & 1;
     if (t + 1 < n_tiles) {
       issue_tile(t + 1, buf ^ 1);
-      if constexpr (C::kLoads == 2) DSA_TILE_BARRIER_VMCNT(2);
-      else DSA_TILE_BARRIER_VMCNT(1);
+      if constexpr (C::kLoads == 4) DSA_TILE_BARRIER_VMCNT(4);
+      else DSA_TILE_BARRIER_VMCNT(2);
     } else {
       DSA_TILE_BARRIER_VMCNT(0);
     }
     const int key0 = glo + t * kKeyTile;
     if (ok && key0 < hi && key0 + kKeyTile > lo) {  // wave-uniform
       const unsigned char* tb = tiles + buf * C::kTileBytes;
-      f32x16 acc[2][2];
+      // one 32-key block at a time: its MFMAs, then its ReLU * w head-sum epilogue, so the
+      // epilogue VALU work can overlap the next block's MFMAs
 #pragma unroll
-      for (int m = 0; m < 2; ++m)
+      for (int nb = 0; nb < kKeyTile / 32; ++nb) {
+        const int n = 32 * nb + l32;
+        f32x16 acc0 = f32x16{}, acc1 = f32x16{};
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) acc[m][nb] = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < kKsteps; ++ks) {
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          const int n = 32 * nb + l32;
+        for (int ks = 0; ks < kKsteps; ++ks) {
           if constexpr (FP8) {
             const int c0 = 4 * ks + 2 * half;  // two 16-byte chunks: d in [64ks + 32half, +32)
-            const i32x4 x0 = *reinterpret_cast<const i32x4*>(tb + n * C::kKeyBytes + kswz(n, c0, C::kChunks) * 16);
-            const i32x4 x1 =
-                *reinterpret_cast<const i32x4*>(tb + n * C::kKeyBytes + kswz(n, c0 + 1, C::kChunks) * 16);
+            const i32x4 x0 = *reinterpret_cast<const i32x4*>(tb + n * C::kKeyBytes + kswz<C::kChunks>(n, c0) * 16);
+            const i32x4 x1 = *reinterpret_cast<const i32x4*>(tb + n * C::kKeyBytes + kswz<C::kChunks>(n, c0 + 1) * 16);
             const i32x8 kb = i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-#pragma unroll
-            for (int m = 0; m < 2; ++m)
-              acc[m][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[m][ks], kb, acc[m][nb], 0, 0, 0, 127,
-                                                                           0, 127);
+            acc0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[0][ks], kb, acc0, 0, 0, 0, 127, 0, 127);
+            acc1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[1][ks], kb, acc1, 0, 0, 0, 127, 0, 127);
           } else {
             const int c = 2 * ks + half;
-            const bf16x8 kb = *reinterpret_cast<const bf16x8*>(tb + n * C::kKeyBytes + kswz(n, c, C::kChunks) * 16);
-#pragma unroll
-            for (int m = 0; m < 2; ++m)
-              acc[m][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[m][ks], kb, acc[m][nb], 0, 0, 0);
+            const bf16x8 kb = *reinterpret_cast<const bf16x8*>(tb + n * C::kKeyBytes + kswz<C::kChunks>(n, c) * 16);
+            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][ks], kb, acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][ks], kb, acc1, 0, 0, 0);
           }
         }
-      }
-      // epilogue: lane holds key 32nb + l32 and heads 32m + 8(r/4) + 4half + r%4
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
+        // lane holds key 32nb + l32 and heads 32m + 8(r/4) + 4half + r%4
         float sacc = 0.f;
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sacc = fmaf(wv[m][r], fmaxf(acc[m][nb][r], 0.f), sacc);
+        for (int r = 0; r < 16; ++r) {
+          sacc = fmaf(wv[0][r], fmaxf(acc0[r], 0.f), sacc);
+          sacc = fmaf(wv[1][r], fmaxf(acc1[r], 0.f), sacc);
+        }
         sacc += __shfl_xor(sacc, 32, 64);
         const int key = key0 + 32 * nb + l32;
         if (half == 0 && key >= lo && key < hi) {
           if constexpr (FP8) sacc *= k_scale[key];
-          scores[int64_t(i) * ld + (key - lo)] = sacc + 0.f;  // -0.0 -> +0.0
+          scores[int64_t(i) * ld + (key - q_origin)] = sacc + 0.f;  // -0.0 -> +0.0
         }
       }
     }
@@ -235,7 +243,7 @@ dsa_status launch_indexer_scores(const dsa_indexer_topk_args* a, float* scores, 
   if (a->nq == 0) return DSA_OK;
   const int stride = a->q_stride, ratio = a->compress_ratio;
   if (a->n_heads == kHi && a->head_dim == kDi && (a->dtype == DSA_BF16 || a->dtype == DSA_FP8_E4M3)) {
-    const dim3 grid((a->nq + kWaves - 1) / kWaves);
+    const dim3 grid((a->nq + kWaves - 1) / kWaves, (max_vis + kChunkKeys - 1) / kChunkKeys);
     if (a->dtype == DSA_BF16) {
       hipLaunchKernelGGL(indexer_mfma<false>, grid, dim3(kThreads), 0, stream,
                          static_cast<const unsigned char*>(a->q_idx), a->q_scale, a->weights,
