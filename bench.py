@@ -37,6 +37,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU time budget of the oracle sample")
     p.add_argument("--profile-only", action="store_true", help="no CPU baseline, fewer prints (for rocprofv3)")
+    p.add_argument("--no-graph", action="store_true", help="time eager ABI calls instead of a captured HIP graph")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain copy of MIB MiB (the rerange kernel in its identity mode) three times; "
                         "its FETCH_SIZE / WRITE_SIZE counters scale the HBM traffic of the other kernels")
@@ -152,16 +153,42 @@ def main():
     if err.item() != 0:
         print(json.dumps({"error": f"device error flag {err.item():#x}"}))
         sys.exit(1)
+    idx_eager, out_eager = idx.clone(), out.clone()
+
+    # The step is captured once into a HIP graph (every kernel of the path, in order, on one
+    # stream) and replayed, so host launch overhead does not sit between the kernels. Each replay
+    # of the timed region is checked bitwise against the eager step (the path is deterministic).
+    graph = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+
+    def run_step():
+        if graph is not None:
+            graph.replay()
+        else:
+            step()
 
     # ---------------- timed region ------------------------------------------------------------
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        step(evs[k])
+        run_step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+    if graph is not None and not (torch.equal(idx, idx_eager) and torch.equal(out.view(torch.int16),
+                                                                          out_eager.view(torch.int16))):
+        print(json.dumps({"error": "graph replay differs from the eager step"}))
+        sys.exit(1)
+
+    # per-ABI-call durations (HIP events on the kernels' stream, eager calls, same work)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
     stage = {name: float(np.mean([e[a].elapsed_time(e[b]) for e in evs]))
              for name, a, b in (("metadata", 0, 1), ("indexer_topk", 1, 2), ("sparse_attn", 2, 3), ("rerange", 3, 4))}
 
@@ -223,6 +250,7 @@ def main():
         "metric": METRIC, "value": tokens_per_s, "unit": "query tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": ak if ik == ak else f"{ak}+{ik}-indexer", "data": "synthetic",
+        "timing": "HIP graph replay of the whole step" if graph is not None else "eager ABI calls",
         "config": {"workload": wl.name, "tokens": wl.T, "requests": len(wl.lens), "cp_size": wl.cp,
                    "cp_rank": wl.rank, "split": wl.mode, "padded": wl.pad, "local_queries": n_real,
                    "heads": wl.H, "d_qk": wl.Dqk, "d_v": wl.Dv, "indexer": f"{wl.Hi}x{wl.Di} {ik}", "topk": wl.topk,
