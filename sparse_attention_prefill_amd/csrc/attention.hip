@@ -153,7 +153,13 @@ constexpr int kLatTile = kTile * kLatBytes;        // 64 KiB
 constexpr int kTileBytes = kLatTile + kTile * kRopeBytes;  // 72 KiB
 constexpr int kMaxKtot = 2304;                     // selected rows per query held in LDS (9 KiB)
 constexpr int kLoadsPerWave = 18;                  // 16 latent rows + 2 rope instructions
-constexpr int kLookK = 2, kLookV = 1;             // LDS operand reads issued ahead of their MFMA
+#ifndef DSA_LOOKK
+#define DSA_LOOKK 3
+#endif
+#ifndef DSA_LOOKV
+#define DSA_LOOKV 2
+#endif
+constexpr int kLookK = DSA_LOOKK, kLookV = DSA_LOOKV;  // LDS operand reads issued ahead of their MFMA
 constexpr float kOverflowMargin = 64.f;            // log2 units: e^(l - m) stays <= 2^64
 
 // LDS tile layout: latent region [64 rows][64 chunks of 16 B], then rope region [64 rows][8
@@ -313,12 +319,11 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
     if (n_tiles > 0) issue_tile(0, 0);
     for (int t = 0; t < n_tiles; ++t) {
       const int buf = t & 1;
-      if (t + 1 < n_tiles) {
-        issue_tile(t + 1, buf ^ 1);
-        DSA_TILE_BARRIER_VMCNT(18);  // this tile landed; the next one (18 loads) stays in flight
-      } else {
-        DSA_TILE_BARRIER_VMCNT(0);
-      }
+      // One barrier per tile: after it, this tile has landed for every wave AND every wave has
+      // finished the previous tile, so the other buffer can take the next tile while this one is
+      // computed.
+      DSA_TILE_BARRIER_VMCNT(0);
+      if (t + 1 < n_tiles) issue_tile(t + 1, buf ^ 1);
       const unsigned char* tb = tiles + buf * kTileBytes;
       const int valid = n_sel - t * kTile;  // real rows in this tile (>= 1)
 
@@ -350,8 +355,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
 
         // lane holds rows n = 32hb + 8(v/4) + 4half + v%4 of head h; mask rows past the selection
         // (only the last tile can be partial: wave-uniform branch)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) s[v] *= scale_log2;
+        // (raw logits; the positive scale is applied inside the exponent below)
         if (valid < kTile) {
           const int lim = valid - 32 * hb - 4 * half;
 #pragma unroll
@@ -361,7 +365,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
         float tmax = -INFINITY;
 #pragma unroll
         for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, s[v]);
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * scale_log2;
         m_seen = fmaxf(m_seen, tmax);
         if (attempt == 0 && t == 0 && hb == 0) {
           // O is still zero: fix the reference max here, no rescale needed
@@ -377,7 +381,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
         for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
           for (int jj = 0; jj < 8; ++jj) {
-            const float p = __builtin_amdgcn_exp2f(s[8 * kk + jj] - m_used);  // v_exp_f32; tiny -> 0
+            const float p = __builtin_amdgcn_exp2f(fmaf(s[8 * kk + jj], scale_log2, -m_used));  // v_exp_f32; tiny -> 0
             psum += p;
             pa[kk][jj] = (__bf16)p;
           }
@@ -412,7 +416,6 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
           __builtin_amdgcn_sched_group_barrier(0x008, kLookV, 0);
         }
       }
-      DSA_TILE_BARRIER_LDS();  // every wave is done with this buffer before it is refilled
     }
     if (attempt == 0) {
       if (__any(overflow) && lane == 0) atomicOr(redo_flag, 1);
