@@ -4,239 +4,719 @@
 // of the local queries over their causal keys) and Implementation §5 (a top-k fed unlocalised
 // metadata collapses to position 0, i.e. the selection is per query over its own extent).
 //
-// One workgroup (1024 threads) per query row:
-//  1. Scores become order-preserving 32-bit keys (-0.0 folded into +0.0).
-//  2. Radix select, 4 passes of 8 bits from the top, finds the K-th largest key tau and how
-//     many keys lie strictly above it; the histograms are LDS atomics.
-//  3. Two LDS bitmaps mark the keys above tau and the keys equal to tau; a block scan over the
-//     bitmap words turns them into positions in ascending order, taking the ties with the lowest
-//     positions (the tie rule: higher score first, then lower key index). The output is thus
-//     deterministic and sorted, with no sort.
-// Rows of up to 1024*EPT keys are held in registers (EPT keys per thread, coalesced 16-byte
-// loads); longer rows are re-read from memory (L2 / MALL) on each pass.
+// One workgroup per query row. Scores become order-preserving 32-bit keys (-0.0 and +0.0 share
+// one key) and a radix select finds the K-th largest key tau in three digits, 12 + 10 + 10 bits.
+// The tie rule (higher score first, then lower key index) is applied exactly: all keys above tau
+// are taken, then the `need` keys equal to tau with the lowest positions. Output ids ascend.
+//
+// Rows of up to NT*EPT keys (topk_reg_kernel) are loaded once into registers, key j of thread t
+// at row position j*NT + t, so one wave instruction covers 64 consecutive positions:
+//   1. a 4096-bin LDS histogram of the top 12 bits; one wave finds the bin b* of the K-th key;
+//   2. the keys inside b* are appended to an LDS list (wave-aggregated) and one wave resolves
+//      the two low digits over that short list (over the registers when b* is too full);
+//   3. per 64-key chunk, ballots count keys above / equal to tau; a block scan over the chunks
+//      gives each chunk's output offset, and a last pass over the registers writes every
+//      selected id at offset + (selected lanes below it): contiguous stores, no sort.
+// Longer rows (topk_stream_kernel) are read from memory once in the common case: a stratified
+// sample of 8192 keys (16 blocks of 512 spread over the row) gives a threshold theta that about
+// 1.6*K keys of the row exceed; one pass appends every key >= theta to the LDS list, the list
+// is selected exactly, and the ids are emitted from LDS bitmaps. When the list ends up with
+// fewer than K keys or overflows, the row falls back to an exact histogram over the whole row
+// (then keys above b* go straight to the bitmaps and only b*'s keys are listed).
 #include "dsa_internal.h"
 
 namespace dsa {
 namespace {
 
-constexpr int kThreads = 1024;
-constexpr int kWaves = kThreads / 64;
-constexpr int kMaxBitmapWords = 131072 / 32;  // rows up to 131072 keys
+constexpr int kMaxRow = 131072;   // longest row (keys)
+constexpr int kBins0 = 4096;      // first digit: key bits 31..20
+constexpr int kBinsR = 1024;      // refinement digits: bits 19..10, then 9..0
+constexpr int kStreamNT = 1024;   // threads of the streamed path (16 waves)
+constexpr int kStreamCand = 5120; // list of the streamed path (two workgroups per CU)
+constexpr int kSampleBlock = 512; // sample keys per wave on the streamed path
+constexpr int kStreamVec = 4;     // float4 loads in flight per thread on the single pass
 
-__device__ inline uint32_t order_key(float f) {
-  uint32_t u = __float_as_uint(f);
-  if (u == 0x80000000u) u = 0;                       // -0.0 == +0.0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);  // larger float -> larger key
+// -0.0 and +0.0 -> 0x80000000; larger float -> larger key; finite floats stay above 2^23.
+__device__ inline uint32_t order_key_bits(uint32_t u) {
+  const uint32_t m = u & 0x7FFFFFFFu;
+  return (u >> 31) ? 0x80000000u - m : 0x80000000u + m;
+}
+__device__ inline uint32_t order_key(float f) { return order_key_bits(__float_as_uint(f)); }
+// the float whose key is k (k >= 2^23, i.e. not a NaN pattern)
+__device__ inline float key_to_float(uint32_t k) {
+  return k >= 0x80000000u ? __uint_as_float(k - 0x80000000u) : __uint_as_float((0x80000000u - k) | 0x80000000u);
 }
 
+__device__ inline uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
+__device__ inline int lanes_below(uint64_t m) {
+  return int(__builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u)));
+}
+// A wave-uniform value the compiler must treat as new: bounds of fully unrolled loops are
+// re-derived per pass, so their per-iteration conditions are not kept alive across passes.
+__device__ inline int opaque(int v) {
+  asm volatile("" : "+s"(v));
+  return v;
+}
+// LDS accesses of this wave issued so far have completed; the compiler moves no access across.
+__device__ inline void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Inclusive scan over the 64 lanes on DPP: shifts by 1, 2, 4, 8 inside each row of 16 lanes,
+// then the last lane of row 0 / row 2 is added to rows 1 / 3 and the last lane of row 1 to rows
+// 2 and 3 (row broadcasts). No LDS round trips.
 __device__ inline int wave_incl_scan(int v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int t = __shfl_up(v, d, 64);
-    if (lane >= d) v += t;
-  }
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
   return v;
 }
 
-// exclusive scan of one int per thread over the block; *total = block sum
+// Exclusive block scan of one int per thread (NW waves); *total = block sum.
+template <int NW>
 __device__ inline int block_excl_scan(int v, int* smem, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int incl = wave_incl_scan(v);
   if (lane == 63) smem[wave] = incl;
   __syncthreads();
   if (wave == 0) {
-    const int x = lane < kWaves ? smem[lane] : 0;
+    const int x = lane < NW ? smem[lane] : 0;
     const int xi = wave_incl_scan(x);
-    if (lane < kWaves) smem[lane] = xi - x;
-    if (lane == kWaves - 1) smem[kWaves] = xi;
+    if (lane < NW) smem[lane] = xi - x;
+    if (lane == NW - 1) smem[NW] = xi;
   }
   __syncthreads();
   const int r = smem[wave] + incl - v;
-  *total = smem[kWaves];
+  *total = smem[NW];
   __syncthreads();
   return r;
 }
 
-struct TopkShared {
-  uint32_t hist[256];
-  uint32_t gt[kMaxBitmapWords];  // keys above tau
-  uint32_t eq[kMaxBitmapWords];  // keys equal to tau
-  int scan[kWaves + 1];
-  uint32_t prefix;
-  int remaining;
-  int tie_count;
+// Two exclusive block scans at once (a and b); smem holds 2*(NW+1) ints.
+template <int NW>
+__device__ inline void block_excl_scan2(int a, int b, int* smem, int* ea, int* eb, int* ta, int* tb) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ia = wave_incl_scan(a), ib = wave_incl_scan(b);
+  if (lane == 63) {
+    smem[wave] = ia;
+    smem[NW + 1 + wave] = ib;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const int x = lane < NW ? smem[lane] : 0, y = lane < NW ? smem[NW + 1 + lane] : 0;
+    const int xi = wave_incl_scan(x), yi = wave_incl_scan(y);
+    if (lane < NW) {
+      smem[lane] = xi - x;
+      smem[NW + 1 + lane] = yi - y;
+    }
+    if (lane == NW - 1) {
+      smem[NW] = xi;
+      smem[2 * NW + 1] = yi;
+    }
+  }
+  __syncthreads();
+  *ea = smem[wave] + ia - a;
+  *eb = smem[NW + 1 + wave] + ib - b;
+  *ta = smem[NW];
+  *tb = smem[2 * NW + 1];
+  __syncthreads();
+}
+
+// One wave: in a complete NBINS-bin histogram, the bin holding the rem-th largest key (counting
+// from the top bin). Lane l first owns bins [NBINS - per*(l+1), NBINS - per*l); the lane whose
+// range holds the target then spreads its bins over the wave. Requires rem <= total.
+template <int NBINS>
+__device__ inline void wave_select(const uint32_t* hist, int rem, int* bin, int* rem_out, int* cnt_out) {
+  constexpr int per = NBINS / 64;
+  static_assert(per % 4 == 0 && per <= 64, "bins per lane");
+  const int lane = threadIdx.x & 63;
+  const int lo = NBINS - per * (lane + 1);
+  int own = 0;
+#pragma unroll
+  for (int k = 0; k < per; k += 4) {
+    const uint4 v = *reinterpret_cast<const uint4*>(hist + lo + k);
+    own += int(v.x + v.y + v.z + v.w);
+  }
+  const int incl = wave_incl_scan(own);
+  const int above = incl - own;
+  const uint64_t m = ballot(above < rem && rem <= incl);
+  const int L = m ? int(__builtin_ctzll(m)) : 63;
+  const int above_L = __builtin_amdgcn_readlane(above, L);
+  const int lo_L = NBINS - per * (L + 1);
+  const int c = lane < per ? int(hist[lo_L + per - 1 - lane]) : 0;  // lane 0: top bin of L
+  const int incl2 = wave_incl_scan(c);
+  const int above2 = above_L + incl2 - c;
+  const uint64_t m2 = ballot(lane < per && above2 < rem && rem <= above2 + c);
+  const int l2 = m2 ? int(__builtin_ctzll(m2)) : 0;
+  *bin = lo_L + per - 1 - l2;
+  *rem_out = rem - __builtin_amdgcn_readlane(above2, l2);
+  *cnt_out = __builtin_amdgcn_readlane(c, l2);
+}
+
+// Zero p[0, n), n a multiple of 4, with NT threads.
+template <int NT>
+__device__ inline void zero_words(uint32_t* p, int n) {
+  for (int b = 4 * threadIdx.x; b < n; b += 4 * NT) *reinterpret_cast<uint4*>(p + b) = uint4{0, 0, 0, 0};
+}
+
+// One wave: resolve the two 10-bit digits below `prefix` (bits 31..20 fixed) over a list of n
+// keys through a 1024-bin LDS histogram; updates prefix and the count still to take.
+__device__ inline void wave_refine_list(const uint32_t* keys, int n, uint32_t* hist, uint32_t* prefix, int* rem) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll 1
+  for (int r = 0; r < 2; ++r) {
+    const int shift = 10 - 10 * r;
+#pragma unroll
+    for (int b = 4 * lane; b < kBinsR; b += 256) *reinterpret_cast<uint4*>(hist + b) = uint4{0, 0, 0, 0};
+    lds_wait();
+    const uint32_t pfx = *prefix >> (shift + 10);
+    for (int c = lane; c < n; c += 64) {
+      const uint32_t key = keys[c];
+      if ((key >> (shift + 10)) == pfx) atomicAdd(&hist[(key >> shift) & (kBinsR - 1)], 1u);
+    }
+    lds_wait();
+    int bin, rem_out, cnt;
+    wave_select<kBinsR>(hist, *rem, &bin, &rem_out, &cnt);
+    *prefix |= uint32_t(bin) << shift;
+    *rem = rem_out;
+    lds_wait();
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Shared row set-up: window rows, short rows, bad rows. Returns false when the row is done.
+// ---------------------------------------------------------------------------------------------
+struct RowInfo {
+  int ev;    // visible keys
+  int base;  // id of position 0
 };
 
-// EPT > 0: keys in registers (positions 4*(j*1024 + tid) + c); EPT == 0: streamed per pass.
-template <int EPT>
-__global__ __launch_bounds__(kThreads, 1) void topk_kernel(
-    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ used_kv,
-    const int32_t* __restrict__ cu_kv, const int32_t* __restrict__ win_kv, int batch, int stride, int ratio, int nq,
-    int max_vis, int K, int window, int kv_row_base, int32_t* __restrict__ out, int32_t* __restrict__ err_flag) {
-  __shared__ TopkShared sh;
-  const int i = blockIdx.x;
-  const int tid = threadIdx.x;
+template <int NT>
+__device__ inline bool row_setup(const int32_t* __restrict__ cu_q, const int32_t* __restrict__ used_kv,
+                                 const int32_t* __restrict__ cu_kv, const int32_t* __restrict__ win_kv, int batch,
+                                 int stride, int ratio, int max_vis, int row_cap, int K, int window, int kv_row_base,
+                                 int32_t* orow, int32_t* err_flag, RowInfo* ri) {
+  const int i = blockIdx.x, tid = threadIdx.x;
   const int k_tot = K + window;
-  int32_t* orow = out + int64_t(i) * k_tot;
-
   QueryView v;
   const bool have = query_view(cu_q, used_kv, cu_kv, batch, stride, i, &v);
   const int ev = have ? (ratio > 1 ? v.E / ratio : v.E) : 0;
-  const bool ok = have && v.E >= 1 && ev <= max_vis;
-  if (!ok) {
+  if (!(have && v.E >= 1 && ev <= max_vis && ev <= row_cap)) {
     if (tid == 0) raise_flag(err_flag, DSA_DEVERR_EXTENT);
-    for (int j = tid; j < k_tot; j += kThreads) orow[j] = -1;
-    return;
+    for (int j = tid; j < k_tot; j += NT) orow[j] = -1;
+    return false;
   }
   // window rows (original tokens): positions max(0, p-window+1) .. p, p = E-1
   if (window > 0) {
     const int p = v.E - 1;
     const int w0 = max(0, p - window + 1);
-    for (int j = tid; j < window; j += kThreads) orow[K + j] = (w0 + j <= p) ? win_kv[v.b] + w0 + j : -1;
+    for (int j = tid; j < window; j += NT) orow[K + j] = (w0 + j <= p) ? win_kv[v.b] + w0 + j : -1;
   }
-  const int base = kv_row_base + v.kv0;
+  ri->ev = ev;
+  ri->base = kv_row_base + v.kv0;
   if (ev <= K) {  // every visible key
-    for (int j = tid; j < K; j += kThreads) orow[j] = j < ev ? base + j : -1;
-    return;
+    for (int j = tid; j < K; j += NT) orow[j] = j < ev ? ri->base + j : -1;
+    return false;
   }
+  return true;
+}
 
-  const float* srow = scores + int64_t(i) * ld;
-  constexpr int kVec = EPT > 0 ? EPT / 4 : 1;
-  uint32_t keys[EPT > 0 ? EPT : 1];
-  if constexpr (EPT > 0) {
+// ---------------------------------------------------------------------------------------------
+// Rows held in registers
+// ---------------------------------------------------------------------------------------------
+template <int NT, int EPT>
+struct RegShared {
+  static constexpr int kWaves = NT / 64;
+  static constexpr int kList = kWaves >= 16 ? 8192 : 4096;
+  static constexpr int kPerWave = kList / kWaves;  // list segment of one wave
+  union {
+    alignas(16) uint32_t hist[kBins0];  // digit 1
+    uint32_t list[kList];               // then: keys of bin b*, (low 20 bits << 12) | chunk
+  } u;
+  alignas(16) uint32_t hist_r[kBinsR];  // digits 2 and 3
+  uint32_t chunk[NT * EPT / 64];        // per 64-key chunk: (#above tau) | (#equal to tau) << 16, then prefix
+  int wave_n[kWaves];                   // keys each wave listed
+  int scan[kWaves + 1];
+  uint32_t prefix;
+  int remaining;
+  bool take_all;
+};
+
+// 1024-thread rows run two workgroups per CU (8 waves per SIMD, at most 64 VGPRs), so one row's
+// loads overlap another row's passes.
+template <int NT, int EPT>
+__global__ __launch_bounds__(NT, NT == 1024 ? 8 : 1) void topk_reg_kernel(
+    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ used_kv,
+    const int32_t* __restrict__ cu_kv, const int32_t* __restrict__ win_kv, int batch, int stride, int ratio,
+    int max_vis, int K, int window, int kv_row_base, int32_t* __restrict__ out, int32_t* __restrict__ err_flag) {
+  static_assert(EPT % 4 == 0 && EPT <= 64, "chunks come in groups of 4; one chunk per lane / thread");
+  using Sh = RegShared<NT, EPT>;
+  __shared__ Sh sh;
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int sel_wave = 0;  // runs the single-wave selects
+  int32_t* orow = out + int64_t(blockIdx.x) * (K + window);
+  RowInfo ri;
+  if (!row_setup<NT>(cu_q, used_kv, cu_kv, win_kv, batch, stride, ratio, max_vis, NT * EPT, K, window, kv_row_base,
+                     orow, err_flag, &ri))
+    return;
+  const int ev = ri.ev;
+  const float* srow = scores + int64_t(blockIdx.x) * ld;
+
+  // Keys. Positions past the row get (lane & 7) << 20: bins 0..7, which hold no finite score,
+  // so they never reach the selection and their histogram atomics spread over 8 addresses.
+  uint32_t keys[EPT];
+  {
+    const int g_load = opaque((ev + 4 * NT - 1) / (4 * NT));
+    float x[EPT];
 #pragma unroll
-    for (int j = 0; j < kVec; ++j) {
-      const int p0 = 4 * (j * kThreads + tid);
-      f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (p0 + 3 < ev) x = *reinterpret_cast<const f32x4*>(srow + p0);
-      else {
+    for (int g = 0; g < EPT / 4; ++g)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) x[c] = p0 + c < ev ? srow[p0 + c] : 0.f;
-      }
+      for (int k = 0; k < 4; ++k) x[4 * g + k] = g < g_load ? srow[min((4 * g + k) * NT + tid, ev - 1)] : 0.f;
+    const uint32_t pad = uint32_t(lane & 7) << 20;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) keys[4 * j + c] = p0 + c < ev ? order_key(x[c]) : 0u;  // 0: not a key
-    }
+    for (int j = 0; j < EPT; ++j) keys[j] = j * NT + tid < ev ? order_key(x[j]) : pad;
   }
-  // visit every valid key: fn(key, position)
-  auto for_each = [&](auto&& fn) {
-    if constexpr (EPT > 0) {
+  // This wave's chunk j covers positions j*NT + wave*64 .. +63. Passes visit the groups of four
+  // chunks whose first chunk starts inside the row; each pass is fully unrolled and tests the
+  // group index against a fresh copy of the scalar bound.
+  const int n_grp = __builtin_amdgcn_readfirstlane(min(EPT / 4, max(0, (ev - wave * 64 + 4 * NT - 1) / (4 * NT))));
+  auto for_chunks = [&](auto&& fn) {
+    const int ng = opaque(n_grp);
 #pragma unroll
-      for (int j = 0; j < kVec; ++j)
+    for (int g = 0; g < EPT / 4; ++g)
+      if (g < ng) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int p = 4 * (j * kThreads + tid) + c;
-          if (p < ev) fn(keys[4 * j + c], p);
-        }
-    } else {
-      for (int p0 = 4 * tid; p0 < ev; p0 += 4 * kThreads) {
-        f32x4 x;
-        if (p0 + 3 < ev) x = *reinterpret_cast<const f32x4*>(srow + p0);
-        else {
-#pragma unroll
-          for (int c = 0; c < 4; ++c) x[c] = p0 + c < ev ? srow[p0 + c] : 0.f;
-        }
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          if (p0 + c < ev) fn(order_key(x[c]), p0 + c);
+        for (int k = 0; k < 4; ++k) fn(4 * g + k);
       }
-    }
   };
 
-  if (tid == 0) {
-    sh.prefix = 0;
-    sh.remaining = K;
+  // ---- digit 1 over the whole row ----
+  zero_words<NT>(sh.u.hist, kBins0);
+  __syncthreads();
+  for_chunks([&](int j) { atomicAdd(&sh.u.hist[keys[j] >> 20], 1u); });
+  __syncthreads();
+  if (wave == sel_wave) {
+    int bin, rem, cnt;
+    wave_select<kBins0>(sh.u.hist, K, &bin, &rem, &cnt);
+    if (lane == 0) {
+      sh.prefix = uint32_t(bin) << 20;
+      sh.remaining = rem;
+      sh.take_all = rem == cnt;  // every key of b* is taken: no lower digits needed
+    }
   }
-  // ---- radix select: the K-th largest key ----
-#pragma unroll 1
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int b = tid; b < 256; b += kThreads) sh.hist[b] = 0;
-    __syncthreads();
-    const uint32_t prefix = sh.prefix;
-    const uint32_t hmask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
-    for_each([&](uint32_t key, int) {
-      if ((key & hmask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
+  zero_words<NT>(sh.hist_r, kBinsR);
+  __syncthreads();
+  const uint32_t bstar = sh.prefix >> 20;
+
+  // ---- one pass: count keys above b* per chunk (lane j of cnt holds chunk j) and list the
+  // keys inside b* in this wave's own segment ----
+  uint32_t* seg = sh.u.list + wave * Sh::kPerWave;
+  {
+    int cnt = 0, n_mine = 0;
+    for_chunks([&](int j) {
+      const uint32_t bin = keys[j] >> 20;
+      const int above = __popcll(ballot(bin > bstar));  // whole-wave vote, outside the select
+      cnt = lane == j ? above : cnt;
+      const bool in_bin = bin == bstar;
+      const uint64_t m = ballot(in_bin);
+      const int slot = n_mine + lanes_below(m);
+      if (in_bin && slot < Sh::kPerWave) seg[slot] = ((keys[j] & 0xFFFFFu) << 12) | uint32_t(j * NW + wave);
+      n_mine += __popcll(m);
     });
-    __syncthreads();
-    if (tid < 64) {
-      // bins 4*lane .. 4*lane+3; suffix sums from the top bin down
-      uint32_t c[4];
+    if (lane < 4 * n_grp) sh.chunk[lane * NW + wave] = uint32_t(cnt);
+    if (lane == 0) sh.wave_n[wave] = n_mine;
+  }
+  __syncthreads();
+  bool listed = true;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) c[k] = sh.hist[4 * tid + k];
-      const int own = int(c[0] + c[1] + c[2] + c[3]);
-      // suffix (inclusive) over lanes: sum of lanes >= tid
-      int suf = own;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int t = __shfl_down(suf, d, 64);
-        if (tid + d < 64) suf += t;
+  for (int w = 0; w < NW; ++w) listed = listed && sh.wave_n[w] <= Sh::kPerWave;
+  const int n_mine = sh.wave_n[wave];
+
+  // ---- digits 2 and 3 (stop as soon as the chosen bin is taken whole) ----
+#pragma unroll 1
+  for (int r = 0; r < 2 && !sh.take_all; ++r) {
+    const int shift = 10 - 10 * r;
+    if (r == 1) {
+      zero_words<NT>(sh.hist_r, kBinsR);
+      __syncthreads();
+    }
+    const uint32_t pfx = sh.prefix >> (shift + 10);
+    if (listed) {  // the list entries share bits 31..20
+      const uint32_t pfx20 = pfx & ((1u << (10 - shift)) - 1u);
+      for (int c = lane; c < n_mine; c += 64) {
+        const uint32_t k20 = seg[c] >> 12;
+        if ((k20 >> (shift + 10)) == pfx20) atomicAdd(&sh.hist_r[(k20 >> shift) & (kBinsR - 1)], 1u);
       }
-      const int above_lane = suf - own;  // keys in bins above this lane's 4 bins
-      const int rem = sh.remaining;
-      int above = above_lane;
-      // the chosen bin b has above(b) < rem <= above(b) + count(b)
-#pragma unroll
-      for (int k = 3; k >= 0; --k) {
-        const int cnt = int(c[k]);
-        if (above < rem && rem <= above + cnt) {
-          sh.prefix = prefix | (uint32_t(4 * tid + k) << shift);
-          sh.remaining = rem - above;
-          sh.tie_count = cnt;
-        }
-        above += cnt;
+    } else {
+      for_chunks([&](int j) {
+        if ((keys[j] >> (shift + 10)) == pfx) atomicAdd(&sh.hist_r[(keys[j] >> shift) & (kBinsR - 1)], 1u);
+      });
+    }
+    __syncthreads();
+    if (wave == sel_wave) {
+      int bin, rem, cnt;
+      wave_select<kBinsR>(sh.hist_r, sh.remaining, &bin, &rem, &cnt);
+      if (lane == 0) {
+        sh.prefix |= uint32_t(bin) << shift;
+        sh.remaining = rem;
+        sh.take_all = rem == cnt;
       }
     }
     __syncthreads();
   }
+  // The selection is every key above tau plus `need` keys equal to it, or, when the last
+  // chosen bin is taken whole, every key >= tau (tau = that bin's lower edge).
   const uint32_t tau = sh.prefix;
-  const int need = sh.remaining;  // ties at tau to take (>= 1)
-  const int n_words = (ev + 31) >> 5;
+  const bool take_all = sh.take_all;
+  const int need = sh.remaining;
 
-  // ---- bitmaps of keys above / equal to tau ----
-  for (int wd = tid; wd < n_words; wd += kThreads) {
-    sh.gt[wd] = 0;
-    sh.eq[wd] = 0;
+  // ---- final per-chunk counts ----
+  if (listed) {  // chunks already hold the keys above b*; add b*'s keys above / at tau
+    const uint32_t tau20 = tau & 0xFFFFFu;
+    for (int c = lane; c < n_mine; c += 64) {
+      const uint32_t e = seg[c], k20 = e >> 12;
+      if (k20 > tau20) atomicAdd(&sh.chunk[e & 0xFFFu], 1u);
+      else if (k20 == tau20) atomicAdd(&sh.chunk[e & 0xFFFu], 1u << 16);
+    }
+  } else {
+    int cnt = 0;
+    for_chunks([&](int j) {
+      const int c = __popcll(ballot(keys[j] > tau)) | (__popcll(ballot(keys[j] == tau)) << 16);
+      cnt = lane == j ? c : cnt;
+    });
+    if (lane < 4 * n_grp) sh.chunk[lane * NW + wave] = uint32_t(cnt);
   }
   __syncthreads();
-  for_each([&](uint32_t key, int p) {
-    if (key > tau) atomicOr(&sh.gt[p >> 5], 1u << (p & 31));
-    else if (key == tau) atomicOr(&sh.eq[p >> 5], 1u << (p & 31));
-  });
+  const int n_chunks = (ev + 63) >> 6;
+  // one scan carries both counts: the low halves sum to at most 32768, so never carry
+  int tot_i;
+  const int v = tid < n_chunks ? int(sh.chunk[tid]) : 0;
+  const int excl = block_excl_scan<NW>(v, sh.scan, &tot_i);
+  if (tid < n_chunks) sh.chunk[tid] = uint32_t(excl);
+  const uint32_t tot = uint32_t(tot_i);
   __syncthreads();
 
-  // ---- ascending positions: each thread owns a contiguous run of words ----
-  const int per = (n_words + kThreads - 1) / kThreads;
-  const int w_begin = min(tid * per, n_words), w_end = min(w_begin + per, n_words);
-  int my_eq = 0;
-  for (int wd = w_begin; wd < w_end; ++wd) my_eq += __popc(sh.eq[wd]);
-  int tot;
-  int eq_rank = block_excl_scan(my_eq, sh.scan, &tot);
-  int my_sel = 0;
-  for (int wd = w_begin; wd < w_end; ++wd) {
-    uint32_t e = sh.eq[wd];
-    // keep only ties with rank < need
-    uint32_t keep = 0;
-    while (e) {
-      const uint32_t bit = e & (~e + 1u);
+  // ---- ordered write: id of each selected key at its chunk's offset + selected lanes below ----
+  const uint32_t pref = lane < 4 * n_grp ? sh.chunk[lane * NW + wave] : 0u;  // lane j: chunk j
+  if (take_all || int(tot >> 16) == need) {  // every key equal to tau is taken
+    for_chunks([&](int j) {
+      const uint32_t pj = __builtin_amdgcn_readlane(pref, j);
+      const bool sel = keys[j] >= tau;
+      const uint64_t s = ballot(sel);
+      if (sel) orow[int(pj & 0xFFFFu) + int(pj >> 16) + lanes_below(s)] = ri.base + j * NT + tid;
+    });
+  } else {  // ties at tau beyond the quota: the lowest positions win
+    for_chunks([&](int j) {
+      const uint32_t pj = __builtin_amdgcn_readlane(pref, j);
+      const int gt_before = int(pj & 0xFFFFu), eq_before = int(pj >> 16);
+      const bool is_eq = keys[j] == tau;
+      const uint64_t e = ballot(is_eq);
+      const bool sel = keys[j] > tau || (is_eq && eq_before + lanes_below(e) < need);
+      const uint64_t s = ballot(sel);
+      if (sel) orow[gt_before + min(eq_before, need) + lanes_below(s)] = ri.base + j * NT + tid;
+    });
+  }
+  const int n_sel = int(tot & 0xFFFFu) + (take_all ? int(tot >> 16) : min(int(tot >> 16), need));
+  for (int j = n_sel + tid; j < K; j += NT) orow[j] = -1;  // only if ties were short (cannot happen)
+}
+
+// ---------------------------------------------------------------------------------------------
+// Rows streamed from memory
+// ---------------------------------------------------------------------------------------------
+struct StreamShared {
+  union {
+    alignas(16) uint32_t hist[kBins0];  // 16 KB, dead once the bitmaps are in use
+    uint64_t bits[2][kMaxRow / 64];     // 32 KB: keys above tau / equal to tau, one bit per position
+  } u;
+  alignas(16) uint32_t hist_r[kBinsR];  // refinement digits
+  uint32_t cand_key[kStreamCand];       // list: keys (raw score bits until the exact select)
+  int32_t cand_pos[kStreamCand];
+  int scan[2 * (kStreamNT / 64 + 1)];
+  uint32_t prefix;
+  int remaining;
+  int n_cand;
+};
+
+__global__ __launch_bounds__(kStreamNT, 8) void topk_stream_kernel(
+    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ used_kv,
+    const int32_t* __restrict__ cu_kv, const int32_t* __restrict__ win_kv, int batch, int stride, int ratio,
+    int max_vis, int K, int window, int kv_row_base, int32_t* __restrict__ out, int32_t* __restrict__ err_flag) {
+  constexpr int NT = kStreamNT, NW = NT / 64;
+  __shared__ StreamShared sh;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int32_t* orow = out + int64_t(blockIdx.x) * (K + window);
+  RowInfo ri;
+  if (!row_setup<NT>(cu_q, used_kv, cu_kv, win_kv, batch, stride, ratio, max_vis, kMaxRow, K, window, kv_row_base,
+                     orow, err_flag, &ri))
+    return;
+  const int ev = ri.ev;
+  const float* srow = scores + int64_t(blockIdx.x) * ld;
+  const int n_chunks = (ev + 63) >> 6;
+  uint64_t* gt = sh.u.bits[0];
+  uint64_t* eq = sh.u.bits[1];
+
+  bool listed = false;
+  if (ev >= NW * 2048) {
+    // ---- sample: wave w reads 512 consecutive keys starting near w*ev/16 ----
+    // (ev >= 16*2048, so the 16 blocks are disjoint and inside the row)
+    uint32_t skey[kSampleBlock / 64];
+    {
+      const int blk = int((int64_t(wave) * ev / NW) & ~int64_t(63));
+#pragma unroll
+      for (int k = 0; k < kSampleBlock / 64; ++k) skey[k] = order_key(srow[blk + 64 * k + lane]);
+    }
+    zero_words<NT>(sh.u.hist, kBins0);
+    zero_words<NT>(sh.hist_r, kBinsR);
+    if (tid == 0) sh.n_cand = 0;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kSampleBlock / 64; ++k) atomicAdd(&sh.u.hist[skey[k] >> 20], 1u);
+    __syncthreads();
+    // the sample rank whose key about 1.6*K keys of the row exceed
+    const int n_sample = NW * kSampleBlock;
+    const int r_s = min(n_sample, int(int64_t(13) * K * n_sample / (int64_t(8) * ev)) + 16);
+    if (wave == 0) {
+      int bin, rem, cnt;
+      wave_select<kBins0>(sh.u.hist, r_s, &bin, &rem, &cnt);
+      if (lane == 0) {
+        sh.prefix = uint32_t(bin) << 20;
+        sh.remaining = rem;
+      }
+    }
+    __syncthreads();
+    {
+      const uint32_t bs = sh.prefix >> 20;
+#pragma unroll
+      for (int k = 0; k < kSampleBlock / 64; ++k)
+        if ((skey[k] >> 20) == bs) atomicAdd(&sh.hist_r[(skey[k] >> 10) & (kBinsR - 1)], 1u);
+    }
+    __syncthreads();
+    if (wave == 0) {
+      int bin, rem, cnt;
+      wave_select<kBinsR>(sh.hist_r, sh.remaining, &bin, &rem, &cnt);
+      if (lane == 0) sh.prefix |= uint32_t(bin) << 10;
+    }
+    __syncthreads();
+    const float theta = key_to_float(sh.prefix);  // key(x) >= prefix  <=>  x >= theta
+    // The single pass compares floats; with theta a normal float that matches the key order
+    // whatever the denormal mode. Otherwise (theta zero or denormal) take the exact path.
+    if (fabsf(theta) >= 1.17549435e-38f) {
+    // ---- single pass: list every key >= theta (raw bits and position) ----
+    const int n_vec = ev >> 2;  // float4s wholly inside the row
+    const int last4 = int(ld >> 2) - 1;
+    const float4* s4 = reinterpret_cast<const float4*>(srow);
+    for (int v0 = 0; v0 * 4 < ev; v0 += NT * kStreamVec) {
+      float4 x[kStreamVec];
+#pragma unroll
+      for (int u = 0; u < kStreamVec; ++u) x[u] = s4[min(v0 + u * NT + tid, last4)];
+      // keys >= theta in this wave's chunks: count, claim their slots with one atomic, place
+      auto listed_key = [&](int u, int c) {
+        const int q = v0 + u * NT + tid;
+        const float xc = c == 0 ? x[u].x : c == 1 ? x[u].y : c == 2 ? x[u].z : x[u].w;
+        return xc >= theta && (q < n_vec || 4 * q + c < ev);
+      };
+      const int n_live = __builtin_amdgcn_readfirstlane(
+          min(kStreamVec, max(0, (((ev + 3) >> 2) - v0 - wave * 64 + NT - 1) / NT)));
+      int total = 0;
+#pragma unroll
+      for (int u = 0; u < kStreamVec; ++u)
+        if (u < n_live)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) total += __popcll(ballot(listed_key(u, c)));
+      if (total == 0) continue;
+      int slot = 0;
+      if (lane == 0) slot = atomicAdd(&sh.n_cand, total);
+      slot = __builtin_amdgcn_readfirstlane(slot);
+      const int nl = opaque(n_live);
+#pragma unroll
+      for (int u = 0; u < kStreamVec; ++u) {
+        if (u >= nl) continue;
+        const int q = v0 + u * NT + tid;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const bool in = listed_key(u, c);
+          const uint64_t m = ballot(in);
+          const int sl = slot + lanes_below(m);
+          if (in && sl < kStreamCand) {
+            sh.cand_key[sl] = __float_as_uint(c == 0 ? x[u].x : c == 1 ? x[u].y : c == 2 ? x[u].z : x[u].w);
+            sh.cand_pos[sl] = 4 * q + c;
+          }
+          slot += __popcll(m);
+        }
+      }
+    }
+    __syncthreads();
+    const int n_cand = sh.n_cand;
+    listed = n_cand >= K && n_cand <= kStreamCand;
+    if (listed) {
+      // ---- exact select over the list: three digits ----
+      for (int c = tid; c < n_cand; c += NT) sh.cand_key[c] = order_key_bits(sh.cand_key[c]);
+      zero_words<NT>(sh.u.hist, kBins0);
+      __syncthreads();
+      for (int c = tid; c < n_cand; c += NT) atomicAdd(&sh.u.hist[sh.cand_key[c] >> 20], 1u);
+      __syncthreads();
+      if (wave == 0) {
+        int bin, rem, cnt;
+        wave_select<kBins0>(sh.u.hist, K, &bin, &rem, &cnt);
+        uint32_t prefix = uint32_t(bin) << 20;
+        wave_refine_list(sh.cand_key, n_cand, sh.hist_r, &prefix, &rem);
+        if (lane == 0) {
+          sh.prefix = prefix;
+          sh.remaining = rem;
+        }
+      }
+      __syncthreads();
+      const uint32_t tau = sh.prefix;
+      for (int c = tid; c < n_chunks; c += NT) gt[c] = eq[c] = 0;
+      __syncthreads();
+      for (int c = tid; c < n_cand; c += NT) {
+        const uint32_t key = sh.cand_key[c];
+        const int p = sh.cand_pos[c];
+        if (key > tau) atomicOr(&gt[p >> 6], 1ull << (p & 63));
+        else if (key == tau) atomicOr(&eq[p >> 6], 1ull << (p & 63));
+      }
+    }
+    }
+  }
+
+  if (!listed) {
+    // ---- exact: digit 1 over the whole row, then b*'s keys ----
+    // visit 64-key chunks of the row in order: fn(key, position, valid), all lanes of a wave
+    auto visit = [&](auto&& fn) {
+      constexpr int U = 8;
+      for (int j0 = 0; j0 * NT < ev; j0 += U) {
+        float x[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) x[u] = srow[min((j0 + u) * NT + tid, ev - 1)];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int p = (j0 + u) * NT + tid;
+          if ((j0 + u) * NT + wave * 64 < ev) fn(order_key(x[u]), p, p < ev);
+        }
+      }
+    };
+    __syncthreads();  // the sampled attempt's LDS reads are done
+    zero_words<NT>(sh.u.hist, kBins0);
+    zero_words<NT>(sh.hist_r, kBinsR);
+    if (tid == 0) sh.n_cand = 0;
+    __syncthreads();
+    visit([&](uint32_t key, int, bool valid) { atomicAdd(&sh.u.hist[valid ? key >> 20 : 0u], 1u); });
+    __syncthreads();
+    if (wave == 0) {
+      int bin, rem, cnt;
+      wave_select<kBins0>(sh.u.hist, K, &bin, &rem, &cnt);
+      if (lane == 0) {
+        sh.prefix = uint32_t(bin) << 20;
+        sh.remaining = rem;
+      }
+    }
+    __syncthreads();
+    const uint32_t bstar = sh.prefix >> 20;
+    for (int c = tid; c < n_chunks; c += NT) eq[c] = 0;
+    visit([&](uint32_t key, int p, bool valid) {
+      const uint32_t bin = key >> 20;
+      const uint64_t g = ballot(valid && bin > bstar);
+      if (lane == 0) gt[p >> 6] = g;
+      const bool in_bin = valid && bin == bstar;
+      const uint64_t cm = ballot(in_bin);
+      if (cm) {
+        int slot = 0;
+        if (lane == 0) slot = atomicAdd(&sh.n_cand, __popcll(cm));
+        slot = __builtin_amdgcn_readfirstlane(slot) + lanes_below(cm);
+        if (in_bin && slot < kStreamCand) {
+          sh.cand_key[slot] = key;
+          sh.cand_pos[slot] = p;
+        }
+      }
+    });
+    __syncthreads();
+    const int n_cand = sh.n_cand;
+    if (n_cand <= kStreamCand) {
+      if (wave == 0) {
+        uint32_t prefix = sh.prefix;
+        int rem = sh.remaining;
+        wave_refine_list(sh.cand_key, n_cand, sh.hist_r, &prefix, &rem);
+        if (lane == 0) {
+          sh.prefix = prefix;
+          sh.remaining = rem;
+        }
+      }
+      __syncthreads();
+      const uint32_t tau = sh.prefix;
+      for (int c = tid; c < n_cand; c += NT) {
+        const uint32_t key = sh.cand_key[c];
+        const int p = sh.cand_pos[c];
+        if (key > tau) atomicOr(&gt[p >> 6], 1ull << (p & 63));
+        else if (key == tau) atomicOr(&eq[p >> 6], 1ull << (p & 63));
+      }
+    } else {  // b* holds more keys than the list: refine and mark over the row itself
+#pragma unroll 1
+      for (int r = 0; r < 2; ++r) {
+        const int shift = 10 - 10 * r;
+        zero_words<NT>(sh.hist_r, kBinsR);
+        __syncthreads();
+        const uint32_t pfx = sh.prefix >> (shift + 10);
+        visit([&](uint32_t key, int, bool valid) {
+          if (valid && (key >> (shift + 10)) == pfx) atomicAdd(&sh.hist_r[(key >> shift) & (kBinsR - 1)], 1u);
+        });
+        __syncthreads();
+        if (wave == 0) {
+          int bin, rem, cnt;
+          wave_select<kBinsR>(sh.hist_r, sh.remaining, &bin, &rem, &cnt);
+          if (lane == 0) {
+            sh.prefix |= uint32_t(bin) << shift;
+            sh.remaining = rem;
+          }
+        }
+        __syncthreads();
+      }
+      const uint32_t tau = sh.prefix;
+      visit([&](uint32_t key, int p, bool valid) {
+        const uint64_t g = ballot(valid && key > tau), e = ballot(valid && key == tau);
+        if (lane == 0) {
+          gt[p >> 6] = g;
+          eq[p >> 6] = e;
+        }
+      });
+    }
+  }
+  __syncthreads();
+  const int need = sh.remaining;  // keys equal to tau to take (>= 1)
+
+  // ---- ascending ids from the bitmaps: each thread owns a run of chunks ----
+  const int per = (n_chunks + NT - 1) / NT;
+  const int c_begin = min(tid * per, n_chunks), c_end = min(c_begin + per, n_chunks);
+  int my_gt = 0, my_eq = 0;
+  for (int c = c_begin; c < c_end; ++c) {
+    my_gt += __popcll(gt[c]);
+    my_eq += __popcll(eq[c]);
+  }
+  int gt_before, eq_before, gt_tot, eq_tot;
+  block_excl_scan2<NW>(my_gt, my_eq, sh.scan, &gt_before, &eq_before, &gt_tot, &eq_tot);
+  int pos = gt_before + min(eq_before, need);
+  int eq_rank = eq_before;
+  for (int c = c_begin; c < c_end; ++c) {
+    uint64_t e = eq[c], keep = 0;
+    while (e) {  // ties in position order, while the quota lasts
+      const uint64_t bit = e & (~e + 1ull);
       if (eq_rank < need) keep |= bit;
       ++eq_rank;
       e ^= bit;
     }
-    sh.eq[wd] = keep | sh.gt[wd];  // final selection bitmap
-    my_sel += __popc(keep | sh.gt[wd]);
-  }
-  int pos = block_excl_scan(my_sel, sh.scan, &tot);
-  for (int wd = w_begin; wd < w_end; ++wd) {
-    uint32_t s = sh.eq[wd];
+    uint64_t s = gt[c] | keep;
     while (s) {
-      const int b = __ffs(s) - 1;
-      if (pos < K) orow[pos] = base + (wd << 5) + b;
+      const int b = __builtin_ctzll(s);
+      if (pos < K) orow[pos] = ri.base + (c << 6) + b;
       ++pos;
       s &= s - 1;
     }
   }
-  for (int j = tot + tid; j < K; j += kThreads) orow[j] = -1;  // only if ties were short (cannot happen)
+  const int n_sel = gt_tot + min(eq_tot, need);
+  for (int j = n_sel + tid; j < K; j += NT) orow[j] = -1;  // only if ties were short (cannot happen)
 }
 
 }  // namespace
@@ -244,18 +724,19 @@ __global__ __launch_bounds__(kThreads, 1) void topk_kernel(
 dsa_status launch_topk(const dsa_indexer_topk_args* a, const float* scores, int64_t ld, int max_vis,
                        hipStream_t stream) {
   if (a->nq == 0) return DSA_OK;
-  if (max_vis > 131072) return fail(DSA_ERR_UNSUPPORTED, "topk: rows longer than 131072 keys");
-  const dim3 grid(a->nq), block(kThreads);
-#define DSA_TOPK_LAUNCH(E)                                                                                       \
-  hipLaunchKernelGGL(topk_kernel<E>, grid, block, 0, stream, scores, ld, a->cu_seqlens_q, a->seqused_kv,       \
-                     a->cu_seqlens_kv, a->window_kv_start, a->batch, a->q_stride, a->compress_ratio, a->nq, max_vis, \
-                     a->topk, a->window, a->kv_row_base, a->topk_idx, a->err_flag)
-  if (max_vis <= 4 * kThreads) DSA_TOPK_LAUNCH(4);
-  else if (max_vis <= 8 * kThreads) DSA_TOPK_LAUNCH(8);
-  else if (max_vis <= 16 * kThreads) DSA_TOPK_LAUNCH(16);
-  else if (max_vis <= 32 * kThreads) DSA_TOPK_LAUNCH(32);
-  else DSA_TOPK_LAUNCH(0);
-#undef DSA_TOPK_LAUNCH
+  if (max_vis > kMaxRow) return fail(DSA_ERR_UNSUPPORTED, "topk: rows longer than 131072 keys");
+  const dim3 grid(a->nq);
+#define DSA_TOPK_ARGS                                                                                          \
+  scores, ld, a->cu_seqlens_q, a->seqused_kv, a->cu_seqlens_kv, a->window_kv_start, a->batch, a->q_stride,     \
+      a->compress_ratio, max_vis, a->topk, a->window, a->kv_row_base, a->topk_idx, a->err_flag
+#define DSA_TOPK_REG(NT, E) hipLaunchKernelGGL((topk_reg_kernel<NT, E>), grid, dim3(NT), 0, stream, DSA_TOPK_ARGS)
+  if (max_vis <= 256 * 16) DSA_TOPK_REG(256, 16);
+  else if (max_vis <= 512 * 16) DSA_TOPK_REG(512, 16);
+  else if (max_vis <= 1024 * 16) DSA_TOPK_REG(1024, 16);
+  else if (max_vis <= 1024 * 32) DSA_TOPK_REG(1024, 32);
+  else hipLaunchKernelGGL(topk_stream_kernel, grid, dim3(kStreamNT), 0, stream, DSA_TOPK_ARGS);
+#undef DSA_TOPK_REG
+#undef DSA_TOPK_ARGS
   return check_launch("topk_kernel");
 }
 

@@ -255,10 +255,12 @@ def score_rows(seed, n_rows, length, kind="normal"):
     """Random fp32 score rows for isolated top-k tests.
 
     kind: "normal" (distinct values), "ties" (few distinct values, many exact ties),
-          "zeros" (mixture of +0.0 and -0.0 and a few positives), "const" (all equal).
+          "zeros" (mixture of +0.0 and -0.0 and a few positives), "const" (all equal),
+          "narrow" (mostly distinct values packed into [1, 1 + 2^-10), so that they share their
+          sign, exponent and leading mantissa bits).
     """
     g = np.random.default_rng(np.random.SeedSequence([seed, T_SCORES, {"normal": 0, "ties": 1, "zeros": 2,
-                                                                     "const": 3}[kind]]))
+                                                                     "const": 3, "narrow": 4}[kind]]))
     if kind == "normal":
         x = g.standard_normal((n_rows, length)).astype(np.float32)
     elif kind == "ties":
@@ -267,6 +269,8 @@ def score_rows(seed, n_rows, length, kind="normal"):
         x = np.where(g.random((n_rows, length)) < 0.5, np.float32(0.0), np.float32(-0.0)).astype(np.float32)
         pos = g.random((n_rows, length)) < 0.01
         x = np.where(pos, g.random((n_rows, length)).astype(np.float32), x).astype(np.float32)
+    elif kind == "narrow":
+        x = (np.float32(1.0) + g.random((n_rows, length)).astype(np.float32) * np.float32(2.0 ** -10)).astype(np.float32)
     else:
         x = np.full((n_rows, length), 1.5, dtype=np.float32)
     return x

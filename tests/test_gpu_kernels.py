@@ -39,13 +39,16 @@ def _run_topk(scores, m, d, K, dev, ratio=1, window=0, win_start=None, kv_row_ba
     return out.cpu().numpy()
 
 
-@pytest.mark.parametrize("kind", ["normal", "ties", "zeros", "const"])
+@pytest.mark.parametrize("kind", ["normal", "ties", "zeros", "const", "narrow"])
 @pytest.mark.parametrize("lens,cp,rank,K", [
     ([700], 1, 0, 64),              # E = 1..700, short rows take everything
-    ([3000], 1, 0, 2048),           # E crosses K; 4-per-thread register path
-    ([9000], 8, 7, 2048),           # 8192 < E <= 9000: 16-per-thread path
-    ([30000], 200, 199, 2048),      # E ~ 30000: 32-per-thread path
-    ([40000], 4000, 3999, 2048),    # E ~ 40000: streamed path
+    ([3000], 1, 0, 2048),           # E crosses K; 256 threads x 16 keys in registers
+    ([6000], 3, 2, 2048),           # 4096 < E <= 6000: 512 x 16 in registers
+    ([9000], 8, 7, 2048),           # 8192 < E <= 9000: 1024 x 16 in registers
+    ([20000], 30, 29, 2048),        # E ~ 20000: 1024 x 32 in registers, two workgroups per CU
+    ([30000], 200, 199, 2048),      # E ~ 30000: 1024 x 32 in registers
+    ([40000], 4000, 3999, 2048),    # E ~ 40000: streamed; "ties", "const" and "narrow" overflow the
+                                    # candidate list and refine over the row itself
     ([131072], 16384, 16383, 2048), # E ~ 131072: streamed path, longest rows
     ([50, 1, 300], 3, 1, 7),        # several requests, round-robin below
 ])
