@@ -60,6 +60,13 @@ __device__ inline void lds_dma16_v(const void* gaddr, uint32_t lds_base) {
                : "memory", "m0");
 }
 
+// per-lane 64-bit global address, 4 bytes: lane l's word lands at lds_base + 4*l
+__device__ inline void lds_dma4_v(const void* gaddr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(gaddr),
+               "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory", "m0");
+}
+
 __device__ inline void raise_flag(int32_t* err_flag, int32_t bits) {
   if (err_flag) atomicOr(err_flag, bits);
 }

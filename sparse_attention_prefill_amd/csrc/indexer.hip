@@ -16,7 +16,8 @@
 //    then applies ReLU, the head weight and the head sum in fp32: the 32x32 accumulator layout
 //    puts one key per lane and 16 heads per lane, so the head sum is 32 in-lane FMAs plus one
 //    cross-half add. Tiles outside a wave's range are skipped by that wave.
-//    fp8: q_scale folds into the head weight and k_scale multiplies the head sum (both > 0).
+//    fp8: q_scale folds into the head weight and k_scale multiplies the head sum (both > 0);
+//    the tile's k_scale values are staged into LDS by the same direct loads as the keys.
 //  * indexer_generic: float32 / bf16, small shapes (VALU, one thread per (query, key)).
 #include "dsa_internal.h"
 
@@ -77,6 +78,11 @@ struct IdxCfg {
   static constexpr int kLoads = kKeyTile * kChunks / kThreads;    // direct loads per lane per tile: 2 or 4
 };
 
+// max(x, 0) on the float's bits: non-negative floats are non-negative ints, and negative floats
+// (-0.0 included) are negative ints, so an integer max with 0 is an exact ReLU in one VALU op
+// (a float max on MFMA results would first canonicalize its input).
+__device__ inline float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 // Physical 16-byte chunk of logical chunk c of key row n in an LDS tile. 256-byte rows (bf16):
 // XOR with n & 15, so the 16 rows read together by one MFMA operand load hit 16 distinct bank
 // groups. 128-byte rows (fp8): a 3-bit XOR chosen so that rows n and n + 8 (which share banks)
@@ -87,14 +93,18 @@ __device__ inline int kswz(int n, int c) {
   else return c ^ (((n >> 1) & 3) | (((n ^ (n >> 3)) & 1) << 2));
 }
 
+// bf16: one workgroup per CU (its 64 x 128 query operand takes 64 VGPRs per lane), with the
+// epilogue software-pipelined against the next block's MFMAs. fp8: two workgroups per CU
+// (4 waves per SIMD, at most 128 VGPRs), which hides more than the pipelining does.
 template <bool FP8>
-__global__ __launch_bounds__(kThreads, 1) void indexer_mfma(
+__global__ __launch_bounds__(kThreads, FP8 ? 4 : 1) void indexer_mfma(
     const unsigned char* __restrict__ qi, const float* __restrict__ q_scale, const float* __restrict__ w,
     const unsigned char* __restrict__ ki, const float* __restrict__ k_scale, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ used_kv, const int32_t* __restrict__ cu_kv, int batch, int stride, int ratio, int nq,
     int nk, int max_vis, float* __restrict__ scores, int64_t ld, int32_t* __restrict__ err_flag) {
   using C = IdxCfg<FP8>;
   __shared__ __attribute__((aligned(16))) unsigned char tiles[2 * C::kTileBytes];
+  __shared__ __attribute__((aligned(16))) float ks_tile[2][FP8 ? kKeyTile : 4];
   __shared__ int s_lo[kWaves], s_hi[kWaves];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -182,25 +192,38 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_mfma(
     }
   };
 
+  // fp8: the tile's per-key scales are staged next to it in LDS: wave w copies keys
+  // [16w, 16w + 16) with one more direct load (16 active lanes of 4 bytes)
+  auto issue_kscale = [&](int t, int buf) {
+    if constexpr (FP8) {
+      if (lane < 16) {
+        const int key = glo + t * kKeyTile + 16 * wave + lane;
+        lds_dma4_v(k_scale + (key < nk ? key : nk - 1), __builtin_amdgcn_readfirstlane(lds_offset(ks_tile[buf] + 16 * wave)));
+      }
+    }
+  };
+  issue_kscale(0, 0);
   issue_tile(0, 0);
   for (int t = 0; t < n_tiles; ++t) {
     const int buf = t & 1;
     if (t + 1 < n_tiles) {
+      issue_kscale(t + 1, buf ^ 1);
       issue_tile(t + 1, buf ^ 1);
-      if constexpr (C::kLoads == 4) DSA_TILE_BARRIER_VMCNT(4);
-      else DSA_TILE_BARRIER_VMCNT(2);
+      // the next tile's loads (and its scales for fp8) may stay in flight
+      if constexpr (FP8) DSA_TILE_BARRIER_VMCNT(3);
+      else DSA_TILE_BARRIER_VMCNT(4);
     } else {
       DSA_TILE_BARRIER_VMCNT(0);
     }
     const int key0 = glo + t * kKeyTile;
     if (ok && key0 < hi && key0 + kKeyTile > lo) {  // wave-uniform
       const unsigned char* tb = tiles + buf * C::kTileBytes;
-      // one 32-key block at a time: its MFMAs, then its ReLU * w head-sum epilogue, so the
-      // epilogue VALU work can overlap the next block's MFMAs
-#pragma unroll
-      for (int nb = 0; nb < kKeyTile / 32; ++nb) {
+      // 32-key blocks; bf16 issues block nb+1's MFMAs before block nb's ReLU * w head-sum
+      // epilogue, so the VALU epilogue runs under the matrix-core work
+      auto block_mfma = [&](int nb, f32x16& a0, f32x16& a1) {
         const int n = 32 * nb + l32;
-        f32x16 acc0 = f32x16{}, acc1 = f32x16{};
+        a0 = f32x16{};
+        a1 = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < kKsteps; ++ks) {
           if constexpr (FP8) {
@@ -208,27 +231,45 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_mfma(
             const i32x4 x0 = *reinterpret_cast<const i32x4*>(tb + n * C::kKeyBytes + kswz<C::kChunks>(n, c0) * 16);
             const i32x4 x1 = *reinterpret_cast<const i32x4*>(tb + n * C::kKeyBytes + kswz<C::kChunks>(n, c0 + 1) * 16);
             const i32x8 kb = i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-            acc0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[0][ks], kb, acc0, 0, 0, 0, 127, 0, 127);
-            acc1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[1][ks], kb, acc1, 0, 0, 0, 127, 0, 127);
+            a0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[0][ks], kb, a0, 0, 0, 0, 127, 0, 127);
+            a1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[1][ks], kb, a1, 0, 0, 0, 127, 0, 127);
           } else {
             const int c = 2 * ks + half;
             const bf16x8 kb = *reinterpret_cast<const bf16x8*>(tb + n * C::kKeyBytes + kswz<C::kChunks>(n, c) * 16);
-            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][ks], kb, acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][ks], kb, acc1, 0, 0, 0);
+            a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][ks], kb, a0, 0, 0, 0);
+            a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][ks], kb, a1, 0, 0, 0);
           }
         }
-        // lane holds key 32nb + l32 and heads 32m + 8(r/4) + 4half + r%4
+      };
+      // lane holds key 32nb + l32 and heads 32m + 8(r/4) + 4half + r%4
+      auto block_epilogue = [&](int nb, const f32x16& a0, const f32x16& a1) {
         float sacc = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          sacc = fmaf(wv[0][r], fmaxf(acc0[r], 0.f), sacc);
-          sacc = fmaf(wv[1][r], fmaxf(acc1[r], 0.f), sacc);
+          sacc = fmaf(wv[0][r], relu_bits(a0[r]), sacc);
+          sacc = fmaf(wv[1][r], relu_bits(a1[r]), sacc);
         }
         sacc += __shfl_xor(sacc, 32, 64);
         const int key = key0 + 32 * nb + l32;
         if (half == 0 && key >= lo && key < hi) {
-          if constexpr (FP8) sacc *= k_scale[key];
+          if constexpr (FP8) sacc *= ks_tile[buf][32 * nb + l32];
           scores[int64_t(i) * ld + (key - q_origin)] = sacc + 0.f;  // -0.0 -> +0.0
+        }
+      };
+      if constexpr (!FP8) {
+        f32x16 acc[2][2];
+        block_mfma(0, acc[0][0], acc[0][1]);
+#pragma unroll
+        for (int nb = 0; nb < kKeyTile / 32; ++nb) {
+          if (nb + 1 < kKeyTile / 32) block_mfma(nb + 1, acc[(nb + 1) & 1][0], acc[(nb + 1) & 1][1]);
+          block_epilogue(nb, acc[nb & 1][0], acc[nb & 1][1]);
+        }
+      } else {
+#pragma unroll
+        for (int nb = 0; nb < kKeyTile / 32; ++nb) {
+          f32x16 acc0, acc1;
+          block_mfma(nb, acc0, acc1);
+          block_epilogue(nb, acc0, acc1);
         }
       }
     }
