@@ -11,7 +11,8 @@
 // Two kernels:
 //  * sparse_attn_mla_bf16: 128 heads x 576 (value = first 512 columns), bf16 in, fp32 accumulate.
 //    One workgroup per query, 4 waves x 32 heads. The selected rows are gathered once per query
-//    into LDS, 64 rows (72 KiB) per tile, double-buffered with direct global->LDS loads; every
+//    into LDS, 64 rows (72 KiB) per tile, double-buffered with direct global->LDS loads that are
+//    issued between the first half-tile's logit MFMAs (one load per two MFMAs); every
 //    wave then runs S^T = K Q^T (32 rows x 32 heads, Q^T held in VGPRs) and O += P V on
 //    32x32x16 bf16 MFMAs. S^T puts one head per lane, so the softmax reductions are in-lane,
 //    and its accumulator layout is directly the A operand of P V (the contraction order over
@@ -153,6 +154,7 @@ constexpr int kLatTile = kTile * kLatBytes;        // 64 KiB
 constexpr int kTileBytes = kLatTile + kTile * kRopeBytes;  // 72 KiB
 constexpr int kMaxKtot = 2304;                     // selected rows per query held in LDS (9 KiB)
 constexpr int kLoadsPerWave = 18;                  // 16 latent rows + 2 rope instructions
+static_assert(kDqk / 32 == kLoadsPerWave, "one gather load per two logit MFMAs of a half-tile");
 #ifndef DSA_LOOKK
 #define DSA_LOOKK 3
 #endif
@@ -183,6 +185,55 @@ __device__ inline s16x4 lds_read_tr16(const unsigned char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
 }
 
+// Selected row ids of query i -> rows[], validated (-1 skipped, out-of-range flagged and
+// skipped) and compacted in order; the tail up to a multiple of `tile` is padded with row 0 (a
+// valid row whose logits are masked). Returns the number of selected rows. All threads call it.
+__device__ inline int compact_rows(const int32_t* __restrict__ idx, int i, int k_tot, int n_rows, int tile, int* rows,
+                                   int* scan, int32_t* err_flag) {
+  constexpr int kPer = kMaxKtot / kThreads;  // 9 entries per thread
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int vals[kPer];
+  int cnt = 0;
+  bool bad = false;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int e = tid * kPer + k;
+    int r = e < k_tot ? idx[int64_t(i) * k_tot + e] : -1;
+    if (r < -1 || r >= n_rows) {
+      bad = true;
+      r = -1;
+    }
+    vals[k] = r;
+    cnt += r >= 0;
+  }
+  if (bad) raise_flag(err_flag, DSA_DEVERR_INDEX);
+  int incl = cnt;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int t = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += t;
+  }
+  if (lane == 63) scan[wave] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += scan[w];
+  if (tid == 0) {
+    int tot = 0;
+    for (int w = 0; w < kWaves; ++w) tot += scan[w];
+    scan[kWaves] = tot;
+  }
+  int pos = base + incl - cnt;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k)
+    if (vals[k] >= 0) rows[pos++] = vals[k];
+  __syncthreads();
+  const int n_sel = scan[kWaves];
+  const int padded = (n_sel + tile - 1) / tile * tile;
+  for (int e = n_sel + tid; e < padded; e += kThreads) rows[e] = 0;
+  __syncthreads();
+  return n_sel;
+}
+
 __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
     const float* __restrict__ sink, uint16_t* __restrict__ out, float* __restrict__ lse,
@@ -199,51 +250,8 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
   const int half = lane >> 5, l32 = lane & 31;
   const int h = wave * 32 + l32;  // this lane's head in S^T / softmax
 
-  // ---- selected row ids -> LDS, validated and compacted (order kept) ----
-  {
-    constexpr int kPer = kMaxKtot / kThreads;  // 9 entries per thread
-    int vals[kPer];
-    int cnt = 0;
-    bool bad = false;
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int e = tid * kPer + k;
-      int r = e < k_tot ? idx[int64_t(i) * k_tot + e] : -1;
-      if (r < -1 || r >= n_rows) {
-        bad = true;
-        r = -1;
-      }
-      vals[k] = r;
-      cnt += r >= 0;
-    }
-    if (bad) raise_flag(err_flag, DSA_DEVERR_INDEX);
-    int incl = cnt;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int t = __shfl_up(incl, d, 64);
-      if (lane >= d) incl += t;
-    }
-    if (lane == 63) scan[wave] = incl;
-    __syncthreads();
-    int base = 0;
-    for (int w = 0; w < wave; ++w) base += scan[w];
-    if (tid == 0) {
-      int tot = 0;
-      for (int w = 0; w < kWaves; ++w) tot += scan[w];
-      scan[kWaves] = tot;
-    }
-    int pos = base + incl - cnt;
-#pragma unroll
-    for (int k = 0; k < kPer; ++k)
-      if (vals[k] >= 0) rows[pos++] = vals[k];
-    __syncthreads();
-    // pad the tail of the last tile with row 0 (a valid row; masked out of the softmax)
-    const int n_sel0 = scan[kWaves];
-    const int padded = (n_sel0 + kTile - 1) / kTile * kTile;
-    for (int e = n_sel0 + tid; e < padded; e += kThreads) rows[e] = 0;
-    __syncthreads();
-  }
-  const int n_sel = scan[kWaves];
+  const int n_sel = compact_rows(idx, i, k_tot, n_rows, kTile, rows, scan, err_flag);
+
   const int n_tiles = (n_sel + kTile - 1) / kTile;
 
   // ---- Q^T operand for S^T = K Q^T: lane holds q[h, 16ks + 8half .. +8) ----
@@ -259,24 +267,35 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
   //          16 B = 1024 B; lane l lands in physical chunk l, i.e. logical chunk l ^ lat_swz(n));
   //  rope:   2 instructions of 8 rows x 8 chunks (lane l: row 8r + l/8, physical chunk l%8).
   const unsigned char* kvb = reinterpret_cast<const unsigned char*>(kv);
-  auto issue_tile = [&](int t, int buf) {
+  // The row ids a wave needs for tile t: lane l holds latent row 16*wave + (l & 15) and, for
+  // the two rope loads, rows 16*wave + 8j + l/8.
+  struct GatherRows {
+    int lat, rope0, rope1;
+  };
+  auto gather_rows = [&](int t) {
+    return GatherRows{rows[t * kTile + 16 * wave + (lane & 15)], rows[t * kTile + 16 * wave + (lane >> 3)],
+                      rows[t * kTile + 16 * wave + 8 + (lane >> 3)]};
+  };
+  // load j (0..kLoadsPerWave-1) of this wave's share of the gather of a tile into buffer buf
+  auto gather_one = [&](const GatherRows& gr, int buf, int j) {
     int lane16 = lane << 4;
     asm volatile("" : "+v"(lane16));  // keep per-lane offsets out of loop-invariant hoisting
     const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_offset(tiles + buf * kTileBytes));
-    const int my_row = rows[t * kTile + 16 * wave + (lane & 15)];  // this wave's 16 latent rows
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int r = __builtin_amdgcn_readlane(my_row, j);
+    if (j < 16) {
+      const int r = __builtin_amdgcn_readlane(gr.lat, j);
       lds_dma16_s(kvb + int64_t(r) * kRowBytes, uint32_t(lane16 ^ (lat_swz(j) << 4)),  // (16w+j)&15 == j
                   dst + uint32_t((16 * wave + j) * kLatBytes));
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n0 = 16 * wave + 8 * j;  // rows n0 + lane/8
-      const int r = rows[t * kTile + n0 + (lane >> 3)];
+    } else {
+      const int n0 = 16 * wave + 8 * (j - 16);  // rows n0 + lane/8
       const int c = (lane & 7) ^ rope_swz(n0 + (lane >> 3));
-      lds_dma16_v(kvb + int64_t(r) * kRowBytes + kLatBytes + (c << 4), dst + uint32_t(kLatTile + n0 * kRopeBytes));
+      lds_dma16_v(kvb + int64_t(j == 16 ? gr.rope0 : gr.rope1) * kRowBytes + kLatBytes + (c << 4),
+                  dst + uint32_t(kLatTile + n0 * kRopeBytes));
     }
+  };
+  auto issue_tile = [&](int t, int buf) {
+    const GatherRows gr = gather_rows(t);
+#pragma unroll
+    for (int j = 0; j < kLoadsPerWave; ++j) gather_one(gr, buf, j);
   };
 
   // per-lane LDS byte offsets (tile-relative). A swizzled chunk offset is (c << 4) ^ (f << 4); the
@@ -305,6 +324,11 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
   f32x16 oacc[kDv / 32];
   float m_used = -INFINITY, l_run = 0.f, m_seen = -INFINITY;
   if (tid == 0) *redo_flag = 0;
+  // Wait here, visibly to the compiler, for the Q^T loads (and the sink load). The tile
+  // barriers are inline asm the compiler does not see through; without this it would place
+  // graded vmcnt waits before the first MFMAs of every tile, which also drain the next tile's
+  // gather loads. Encoding: vmcnt(0), expcnt and lgkmcnt left at their maximum.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
 
 #pragma unroll 1
   for (int attempt = 0; attempt < 2; ++attempt) {
@@ -323,7 +347,10 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
       // finished the previous tile, so the other buffer can take the next tile while this one is
       // computed.
       DSA_TILE_BARRIER_VMCNT(0);
-      if (t + 1 < n_tiles) issue_tile(t + 1, buf ^ 1);
+      // the next tile's gather is issued inside the first half-tile's logit MFMAs (one load per
+      // two MFMAs), so in-order issue does not hold the matrix core while the loads queue up
+      const bool gather_next = t + 1 < n_tiles;
+      const GatherRows gr = gather_next ? gather_rows(t + 1) : GatherRows{0, 0, 0};
       const unsigned char* tb = tiles + buf * kTileBytes;
       const int valid = n_sel - t * kTile;  // real rows in this tile (>= 1)
 
@@ -331,7 +358,29 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
       for (int hb = 0; hb < 2; ++hb) {  // 32-row halves of the tile
         // S^T[n][h] = K[n,:] . Q[h,:] for rows n = 32hb + 0..31
         f32x16 s = f32x16{};
-        {
+        if (hb == 0 && gather_next) {
+          // explicit software pipeline: kLookK operand reads ahead; after every second MFMA one
+          // gather load (its memory clobber keeps the operand reads in this order)
+          int k_x = k_x0, r_x = r_x0;
+          asm volatile("" : "+v"(k_x), "+v"(r_x));
+          auto k_read = [&](int ks) {
+            return ks < kDv / 16 ? *reinterpret_cast<const bf16x8*>(tb + k_base + ((32 * ks) ^ k_x))
+                                 : *reinterpret_cast<const bf16x8*>(tb + r_base + ((32 * (ks - kDv / 16)) ^ r_x));
+          };
+          bf16x8 a[kDqk / 16];
+#pragma unroll
+          for (int ks = 0; ks < kLookK; ++ks) a[ks] = k_read(ks);
+#pragma unroll
+          for (int c = 0; c < kDqk / 32; ++c) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const int ks = 2 * c + u;
+              if (ks + kLookK < kDqk / 16) a[ks + kLookK] = k_read(ks + kLookK);
+              s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], qreg[ks], s, 0, 0, 0);
+            }
+            gather_one(gr, buf ^ 1, c);
+          }
+        } else {
           int k_x = k_x0, r_x = r_x0;
           asm volatile("" : "+v"(k_x), "+v"(r_x));  // recomputed per half-tile: no hoisting of 36 offsets
           bf16x8 a[kDqk / 16];
@@ -436,6 +485,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
   }
   if (lse && half == 0) lse[int64_t(i) * kH + h] = l_run > 0.f ? (m_used + log2f(l_run)) / kLog2e : -INFINITY;
 }
+
 
 }  // namespace
 

@@ -19,6 +19,8 @@
 //    fp8: q_scale folds into the head weight and k_scale multiplies the head sum (both > 0);
 //    the tile's k_scale values are staged into LDS by the same direct loads as the keys.
 //  * indexer_generic: float32 / bf16, small shapes (VALU, one thread per (query, key)).
+#include <algorithm>
+
 #include "dsa_internal.h"
 
 namespace dsa {
@@ -68,7 +70,8 @@ __global__ __launch_bounds__(kGenThreads) void indexer_generic(
 constexpr int kHi = 64, kDi = 128;
 constexpr int kWaves = 8, kThreads = kWaves * 64;
 constexpr int kKeyTile = 128;
-constexpr int kChunkKeys = 16 * kKeyTile;  // keys per workgroup (grid.y splits longer ranges)
+constexpr int kChunkKeys = 16 * kKeyTile;  // smallest key chunk per workgroup (grid.y splits longer ranges)
+constexpr int kTargetWorkgroups = 2048;    // chunks grow until the grid is about this large
 
 template <bool FP8>
 struct IdxCfg {
@@ -101,7 +104,7 @@ __global__ __launch_bounds__(kThreads, FP8 ? 4 : 1) void indexer_mfma(
     const unsigned char* __restrict__ qi, const float* __restrict__ q_scale, const float* __restrict__ w,
     const unsigned char* __restrict__ ki, const float* __restrict__ k_scale, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ used_kv, const int32_t* __restrict__ cu_kv, int batch, int stride, int ratio, int nq,
-    int nk, int max_vis, float* __restrict__ scores, int64_t ld, int32_t* __restrict__ err_flag) {
+    int nk, int max_vis, int chunk_keys, float* __restrict__ scores, int64_t ld, int32_t* __restrict__ err_flag) {
   using C = IdxCfg<FP8>;
   __shared__ __attribute__((aligned(16))) unsigned char tiles[2 * C::kTileBytes];
   __shared__ __attribute__((aligned(16))) float ks_tile[2][FP8 ? kKeyTile : 4];
@@ -132,19 +135,16 @@ __global__ __launch_bounds__(kThreads, FP8 ? 4 : 1) void indexer_mfma(
     s_hi[wave] = ok && hi > lo ? hi : INT32_MIN;
   }
   __syncthreads();
-  int glo = INT32_MAX, ghi = INT32_MIN;
+  int ulo = INT32_MAX, uhi = INT32_MIN;  // union of the 8 queries' key ranges
 #pragma unroll
   for (int k = 0; k < kWaves; ++k) {
-    glo = min(glo, s_lo[k]);
-    ghi = max(ghi, s_hi[k]);
+    ulo = min(ulo, s_lo[k]);
+    uhi = max(uhi, s_hi[k]);
   }
-  // this workgroup's slice of the union key range: chunk blockIdx.y
-  glo = glo + int(blockIdx.y) * kChunkKeys;
-  ghi = min(ghi, glo + kChunkKeys);
-  if (ghi <= glo) return;  // uniform: nothing to score in this workgroup
-  lo = max(lo, glo);
-  hi = min(hi, ghi);
-  const int n_tiles = (ghi - glo + kKeyTile - 1) / kKeyTile;
+  // The union is cut into chunks of chunk_keys keys; workgroup y takes chunks y, y + gridDim.y,
+  // ... A union can be longer than the longest single range (queries of two requests), so the
+  // grid-stride loop, not the grid size, guarantees that every chunk is covered.
+  if (uhi <= ulo || int64_t(blockIdx.y) * chunk_keys >= int64_t(uhi) - ulo) return;  // uniform
 
   // ---- A operand: this wave's query block, heads 32m + l32, d-slices per k-step ----
   constexpr int kKsteps = FP8 ? kDi / 64 : kDi / 16;  // 2 or 8
@@ -175,105 +175,112 @@ __global__ __launch_bounds__(kThreads, FP8 ? 4 : 1) void indexer_mfma(
     }
   }
 
-  // ---- staging: tile t holds keys glo + 64t + [0,64); lane loads 16-byte chunks ----
-  auto issue_tile = [&](int t, int buf) {
-    unsigned char* dst = tiles + buf * C::kTileBytes;
+#pragma unroll 1
+  for (int64_t cs = int64_t(blockIdx.y) * chunk_keys; cs < int64_t(uhi) - ulo; cs += int64_t(gridDim.y) * chunk_keys) {
+    const int glo = ulo + int(cs);
+    const int ghi = int(min(int64_t(uhi), int64_t(glo) + chunk_keys));
+    const int lo_c = max(lo, glo), hi_c = min(hi, ghi);
+    const int n_tiles = (ghi - glo + kKeyTile - 1) / kKeyTile;
+    // ---- staging: tile t holds keys glo + 128t + [0, 128); lane loads 16-byte chunks ----
+    auto issue_tile = [&](int t, int buf) {
+      unsigned char* dst = tiles + buf * C::kTileBytes;
 #pragma unroll
-    for (int j = 0; j < C::kLoads; ++j) {
-      const int f0 = 64 * (C::kLoads * wave + j);
-      const int f = f0 + lane;
-      const int n = f / C::kChunks;
-      const int cp = f - n * C::kChunks;
-      const int c = kswz<C::kChunks>(n, cp);
-      int row = glo + t * kKeyTile + n;
-      row = row < nk ? row : nk - 1;
-      const unsigned char* src = ki + int64_t(row) * C::kKeyBytes + c * 16;
-      lds_dma16_v(src, __builtin_amdgcn_readfirstlane(lds_offset(dst + f0 * 16)));
-    }
-  };
-
-  // fp8: the tile's per-key scales are staged next to it in LDS: wave w copies keys
-  // [16w, 16w + 16) with one more direct load (16 active lanes of 4 bytes)
-  auto issue_kscale = [&](int t, int buf) {
-    if constexpr (FP8) {
-      if (lane < 16) {
-        const int key = glo + t * kKeyTile + 16 * wave + lane;
-        lds_dma4_v(k_scale + (key < nk ? key : nk - 1), __builtin_amdgcn_readfirstlane(lds_offset(ks_tile[buf] + 16 * wave)));
+      for (int j = 0; j < C::kLoads; ++j) {
+        const int f0 = 64 * (C::kLoads * wave + j);
+        const int f = f0 + lane;
+        const int n = f / C::kChunks;
+        const int cp = f - n * C::kChunks;
+        const int c = kswz<C::kChunks>(n, cp);
+        int row = glo + t * kKeyTile + n;
+        row = row < nk ? row : nk - 1;
+        const unsigned char* src = ki + int64_t(row) * C::kKeyBytes + c * 16;
+        lds_dma16_v(src, __builtin_amdgcn_readfirstlane(lds_offset(dst + f0 * 16)));
       }
-    }
-  };
-  issue_kscale(0, 0);
-  issue_tile(0, 0);
-  for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < n_tiles) {
-      issue_kscale(t + 1, buf ^ 1);
-      issue_tile(t + 1, buf ^ 1);
-      // the next tile's loads (and its scales for fp8) may stay in flight
-      if constexpr (FP8) DSA_TILE_BARRIER_VMCNT(3);
-      else DSA_TILE_BARRIER_VMCNT(4);
-    } else {
-      DSA_TILE_BARRIER_VMCNT(0);
-    }
-    const int key0 = glo + t * kKeyTile;
-    if (ok && key0 < hi && key0 + kKeyTile > lo) {  // wave-uniform
-      const unsigned char* tb = tiles + buf * C::kTileBytes;
-      // 32-key blocks; bf16 issues block nb+1's MFMAs before block nb's ReLU * w head-sum
-      // epilogue, so the VALU epilogue runs under the matrix-core work
-      auto block_mfma = [&](int nb, f32x16& a0, f32x16& a1) {
-        const int n = 32 * nb + l32;
-        a0 = f32x16{};
-        a1 = f32x16{};
+    };
+
+    // fp8: the tile's per-key scales are staged next to it in LDS: wave w copies keys
+    // [16w, 16w + 16) with one more direct load (16 active lanes of 4 bytes)
+    auto issue_kscale = [&](int t, int buf) {
+      if constexpr (FP8) {
+        if (lane < 16) {
+          const int key = glo + t * kKeyTile + 16 * wave + lane;
+          lds_dma4_v(k_scale + (key < nk ? key : nk - 1), __builtin_amdgcn_readfirstlane(lds_offset(ks_tile[buf] + 16 * wave)));
+        }
+      }
+    };
+    issue_kscale(0, 0);
+    issue_tile(0, 0);
+    for (int t = 0; t < n_tiles; ++t) {
+      const int buf = t & 1;
+      if (t + 1 < n_tiles) {
+        issue_kscale(t + 1, buf ^ 1);
+        issue_tile(t + 1, buf ^ 1);
+        // the next tile's loads (and its scales for fp8) may stay in flight
+        if constexpr (FP8) DSA_TILE_BARRIER_VMCNT(3);
+        else DSA_TILE_BARRIER_VMCNT(4);
+      } else {
+        DSA_TILE_BARRIER_VMCNT(0);
+      }
+      const int key0 = glo + t * kKeyTile;
+      if (ok && key0 < hi_c && key0 + kKeyTile > lo_c) {  // wave-uniform
+        const unsigned char* tb = tiles + buf * C::kTileBytes;
+        // 32-key blocks; bf16 issues block nb+1's MFMAs before block nb's ReLU * w head-sum
+        // epilogue, so the VALU epilogue runs under the matrix-core work
+        auto block_mfma = [&](int nb, f32x16& a0, f32x16& a1) {
+          const int n = 32 * nb + l32;
+          a0 = f32x16{};
+          a1 = f32x16{};
 #pragma unroll
-        for (int ks = 0; ks < kKsteps; ++ks) {
-          if constexpr (FP8) {
-            const int c0 = 4 * ks + 2 * half;  // two 16-byte chunks: d in [64ks + 32half, +32)
-            const i32x4 x0 = *reinterpret_cast<const i32x4*>(tb + n * C::kKeyBytes + kswz<C::kChunks>(n, c0) * 16);
-            const i32x4 x1 = *reinterpret_cast<const i32x4*>(tb + n * C::kKeyBytes + kswz<C::kChunks>(n, c0 + 1) * 16);
-            const i32x8 kb = i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-            a0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[0][ks], kb, a0, 0, 0, 0, 127, 0, 127);
-            a1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[1][ks], kb, a1, 0, 0, 0, 127, 0, 127);
-          } else {
-            const int c = 2 * ks + half;
-            const bf16x8 kb = *reinterpret_cast<const bf16x8*>(tb + n * C::kKeyBytes + kswz<C::kChunks>(n, c) * 16);
-            a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][ks], kb, a0, 0, 0, 0);
-            a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][ks], kb, a1, 0, 0, 0);
+          for (int ks = 0; ks < kKsteps; ++ks) {
+            if constexpr (FP8) {
+              const int c0 = 4 * ks + 2 * half;  // two 16-byte chunks: d in [64ks + 32half, +32)
+              const i32x4 x0 = *reinterpret_cast<const i32x4*>(tb + n * C::kKeyBytes + kswz<C::kChunks>(n, c0) * 16);
+              const i32x4 x1 = *reinterpret_cast<const i32x4*>(tb + n * C::kKeyBytes + kswz<C::kChunks>(n, c0 + 1) * 16);
+              const i32x8 kb = i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+              a0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[0][ks], kb, a0, 0, 0, 0, 127, 0, 127);
+              a1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[1][ks], kb, a1, 0, 0, 0, 127, 0, 127);
+            } else {
+              const int c = 2 * ks + half;
+              const bf16x8 kb = *reinterpret_cast<const bf16x8*>(tb + n * C::kKeyBytes + kswz<C::kChunks>(n, c) * 16);
+              a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][ks], kb, a0, 0, 0, 0);
+              a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][ks], kb, a1, 0, 0, 0);
+            }
+          }
+        };
+        // lane holds key 32nb + l32 and heads 32m + 8(r/4) + 4half + r%4
+        auto block_epilogue = [&](int nb, const f32x16& a0, const f32x16& a1) {
+          float sacc = 0.f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            sacc = fmaf(wv[0][r], relu_bits(a0[r]), sacc);
+            sacc = fmaf(wv[1][r], relu_bits(a1[r]), sacc);
+          }
+          sacc += __shfl_xor(sacc, 32, 64);
+          const int key = key0 + 32 * nb + l32;
+          if (half == 0 && key >= lo_c && key < hi_c) {
+            if constexpr (FP8) sacc *= ks_tile[buf][32 * nb + l32];
+            scores[int64_t(i) * ld + (key - q_origin)] = sacc + 0.f;  // -0.0 -> +0.0
+          }
+        };
+        if constexpr (!FP8) {
+          f32x16 acc[2][2];
+          block_mfma(0, acc[0][0], acc[0][1]);
+#pragma unroll
+          for (int nb = 0; nb < kKeyTile / 32; ++nb) {
+            if (nb + 1 < kKeyTile / 32) block_mfma(nb + 1, acc[(nb + 1) & 1][0], acc[(nb + 1) & 1][1]);
+            block_epilogue(nb, acc[nb & 1][0], acc[nb & 1][1]);
+          }
+        } else {
+#pragma unroll
+          for (int nb = 0; nb < kKeyTile / 32; ++nb) {
+            f32x16 acc0, acc1;
+            block_mfma(nb, acc0, acc1);
+            block_epilogue(nb, acc0, acc1);
           }
         }
-      };
-      // lane holds key 32nb + l32 and heads 32m + 8(r/4) + 4half + r%4
-      auto block_epilogue = [&](int nb, const f32x16& a0, const f32x16& a1) {
-        float sacc = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          sacc = fmaf(wv[0][r], relu_bits(a0[r]), sacc);
-          sacc = fmaf(wv[1][r], relu_bits(a1[r]), sacc);
-        }
-        sacc += __shfl_xor(sacc, 32, 64);
-        const int key = key0 + 32 * nb + l32;
-        if (half == 0 && key >= lo && key < hi) {
-          if constexpr (FP8) sacc *= ks_tile[buf][32 * nb + l32];
-          scores[int64_t(i) * ld + (key - q_origin)] = sacc + 0.f;  // -0.0 -> +0.0
-        }
-      };
-      if constexpr (!FP8) {
-        f32x16 acc[2][2];
-        block_mfma(0, acc[0][0], acc[0][1]);
-#pragma unroll
-        for (int nb = 0; nb < kKeyTile / 32; ++nb) {
-          if (nb + 1 < kKeyTile / 32) block_mfma(nb + 1, acc[(nb + 1) & 1][0], acc[(nb + 1) & 1][1]);
-          block_epilogue(nb, acc[nb & 1][0], acc[nb & 1][1]);
-        }
-      } else {
-#pragma unroll
-        for (int nb = 0; nb < kKeyTile / 32; ++nb) {
-          f32x16 acc0, acc1;
-          block_mfma(nb, acc0, acc1);
-          block_epilogue(nb, acc0, acc1);
-        }
       }
+      DSA_TILE_BARRIER_LDS();
     }
-    DSA_TILE_BARRIER_LDS();
   }
 }
 
@@ -284,17 +291,22 @@ dsa_status launch_indexer_scores(const dsa_indexer_topk_args* a, float* scores, 
   if (a->nq == 0) return DSA_OK;
   const int stride = a->q_stride, ratio = a->compress_ratio;
   if (a->n_heads == kHi && a->head_dim == kDi && (a->dtype == DSA_BF16 || a->dtype == DSA_FP8_E4M3)) {
-    const dim3 grid((a->nq + kWaves - 1) / kWaves, (max_vis + kChunkKeys - 1) / kChunkKeys);
+    // chunks of 2048 keys fill the GPU for short query batches; long batches take larger chunks
+    // (fewer reloads of each group's query block, fewer workgroup start-ups)
+    const int64_t groups = (a->nq + kWaves - 1) / kWaves, base_chunks = (max_vis + kChunkKeys - 1) / kChunkKeys;
+    const int64_t merge = std::max<int64_t>(1, groups * base_chunks / kTargetWorkgroups);
+    const int chunk_keys = int(std::min<int64_t>(merge, base_chunks) * kChunkKeys);
+    const dim3 grid(unsigned(groups), unsigned((max_vis + chunk_keys - 1) / chunk_keys));
     if (a->dtype == DSA_BF16) {
       hipLaunchKernelGGL(indexer_mfma<false>, grid, dim3(kThreads), 0, stream,
                          static_cast<const unsigned char*>(a->q_idx), a->q_scale, a->weights,
                          static_cast<const unsigned char*>(a->k_idx), a->k_scale, a->cu_seqlens_q, a->seqused_kv,
-                         a->cu_seqlens_kv, a->batch, stride, ratio, a->nq, a->nk, max_vis, scores, ld, a->err_flag);
+                         a->cu_seqlens_kv, a->batch, stride, ratio, a->nq, a->nk, max_vis, chunk_keys, scores, ld, a->err_flag);
     } else {
       hipLaunchKernelGGL(indexer_mfma<true>, grid, dim3(kThreads), 0, stream,
                          static_cast<const unsigned char*>(a->q_idx), a->q_scale, a->weights,
                          static_cast<const unsigned char*>(a->k_idx), a->k_scale, a->cu_seqlens_q, a->seqused_kv,
-                         a->cu_seqlens_kv, a->batch, stride, ratio, a->nq, a->nk, max_vis, scores, ld, a->err_flag);
+                         a->cu_seqlens_kv, a->batch, stride, ratio, a->nq, a->nk, max_vis, chunk_keys, scores, ld, a->err_flag);
     }
     return check_launch("indexer_mfma");
   }

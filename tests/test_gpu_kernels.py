@@ -143,6 +143,10 @@ def _indexer_case(wl, variant, dev, rows_cap=None):
     ("rr_cp8_r3_batch4", {"lens": (1500, 700, 130, 5)}),
     ("long_131k_fp8", {"lens": (3000,)}),
     ("rr_cp4_r1_var8_cmp4", {"lens": (1100, 1900, 13, 640)}),
+    # groups of 8 queries that straddle a request boundary: their union key range is longer than
+    # any single range and ends just past a multiple of the 2048-key chunk
+    ("inseq_cp8_last_8k", {"lens": (2046, 3), "cp": 2, "rank": 1}),
+    ("long_131k_fp8", {"lens": (2045, 50), "cp": 8, "rank": 7}),
 ])
 def test_indexer_scores(name, kw, variant):
     dev = gpu()
