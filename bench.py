@@ -77,7 +77,7 @@ def main():
 
     # ---------------- setup (untimed): inputs for the rank's tokens, resident in HBM -------------
     qsl_d = torch.tensor(wl.qsl, dtype=torch.int32, device=dev)
-    lens_d = torch.tensor(np.asarray(wl.lens), dtype=torch.int32, device=dev)
+    lens_d = torch.tensor(wl.seq_lens, dtype=torch.int32, device=dev)
     tpr, n_real, rows_concat = D.cp_sizes(wl.T, wl.cp, wl.rank, mode, wl.pad)
     meta0 = D.build_cp_metadata(qsl_d, lens_d, wl.T, wl.cp, wl.rank, mode, wl.pad)
     torch.cuda.synchronize()
@@ -101,7 +101,7 @@ def main():
     k_scale = dev_t(inp["k_scale"], "f32") if "k_scale" in inp else None
     q_d, kv_d, sink_d = dev_t(qin["q"], ak), dev_t(inp["kv"], ak), dev_t(inp["sink"], "f32")
     kv_cmp = dev_t(inp["kv_cmp_start"], "i32") if wl.compress > 1 else None
-    max_kv = max(wl.lens)
+    max_kv = int(wl.seq_lens.max())
     scale = 1.0 / np.sqrt(wl.Dqk)
     # outputs / workspace, allocated once
     meta = {k: torch.empty_like(v) if v is not None else None for k, v in meta0.items()}
@@ -111,7 +111,7 @@ def main():
     stride = wl.cp if wl.mode == "round_robin" else 1
 
     def ikw(m):
-        return dict(topk=wl.topk, q_stride=stride, compress_ratio=wl.compress, kv_row_base=wl.T if wl.compress > 1 else 0,
+        return dict(topk=wl.topk, q_stride=stride, compress_ratio=wl.compress, kv_row_base=wl.n_kv if wl.compress > 1 else 0,
                     window=wl.window, window_kv_start=m["local_kv_start_loc"] if wl.window else None,
                     q_scale=q_scale, k_scale=k_scale, err_flag=err)
 
@@ -252,6 +252,7 @@ def main():
         "vs_baseline": None, "dtype": ak if ik == ak else f"{ak}+{ik}-indexer", "data": "synthetic",
         "timing": "HIP graph replay of the whole step" if graph is not None else "eager ABI calls",
         "config": {"workload": wl.name, "tokens": wl.T, "requests": len(wl.lens), "cp_size": wl.cp,
+                   "cached_prefix_tokens": int(wl.n_kv - wl.T),
                    "cp_rank": wl.rank, "split": wl.mode, "padded": wl.pad, "local_queries": n_real,
                    "heads": wl.H, "d_qk": wl.Dqk, "d_v": wl.Dv, "indexer": f"{wl.Hi}x{wl.Di} {ik}", "topk": wl.topk,
                    "window": wl.window, "compress": wl.compress},
@@ -282,7 +283,7 @@ def cpu_baseline(wl, meta_np, inp, qin, budget_s):
         cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
         cores = len(os.sched_getaffinity(0))
-    m = O.cp_metadata(wl.qsl, wl.lens, wl.cp, wl.rank, wl.mode, wl.pad)
+    m = O.cp_metadata(wl.qsl, wl.seq_lens, wl.cp, wl.rank, wl.mode, wl.pad)
     n = m["n_local_real"]
     order = np.random.default_rng(0).permutation(n)
     done = 0

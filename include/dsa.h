@@ -56,7 +56,7 @@ typedef enum {
 /* Device-side error bits written to *err_flag. */
 #define DSA_DEVERR_QSL_START 0x1      /* query_start_loc[0] != 0                                 */
 #define DSA_DEVERR_QSL_ORDER 0x2      /* query_start_loc decreasing                              */
-#define DSA_DEVERR_NOT_PREFILL 0x4    /* seq_lens[b] != query length (chunked prefill, later)   */
+#define DSA_DEVERR_SEQ_LENS 0x4       /* seq_lens[b] < query length of request b                 */
 #define DSA_DEVERR_QSL_TOTAL 0x8      /* query_start_loc[B] != num_tokens                        */
 #define DSA_DEVERR_ROWS 0x10          /* local cu_seqlens_q[B] != nq (global metadata passed?)   */
 #define DSA_DEVERR_EXTENT 0x20        /* a query's causal extent is outside the key buffer       */
@@ -86,21 +86,28 @@ dsa_status dsa_cp_sizes(int32_t num_tokens, int32_t cp_size, int32_t cp_rank, in
  * (1) CP-local metadata ([xLLM-CP] Implementation §2, build of the CP-local metadata; Design,
  * key points: local queries see a right-aligned KV extent and the last rank sees the whole
  * stream; [CP-blog] §2B: after the round-robin scatter the per-rank sequence lengths and
- * cu-seqlens are recomputed).
+ * cu-seqlens are recomputed; [xLLM-CP] Testing: chunked prefill is part of the functional
+ * matrix).
  *
  * In (device): query_start_loc [batch+1] (global cu-seqlens of the flattened query stream),
- *              seq_lens [batch] (must equal the query lengths: pure prefill).
+ *              seq_lens [batch] (KV tokens of each request, >= its query length n_b).
+ * Chunked prefill: request b carries P_b = seq_lens[b] - n_b cached tokens. Its KV segment is
+ * seq_lens[b] rows long, prefix first, and the segments follow one another in request order
+ * (segment b starts at row sum_{b'<b} seq_lens[b']). Query g (0-based) of request b sits at
+ * KV position P_b + g. Pure prefill is P_b = 0 for every request.
  * Out (device):
  *   local_query_start_loc [batch+1]  cu-seqlens of the rank's real local queries per request
  *   local_seq_lens        [batch]    KV extent seen by the request's last local query
- *                                    (in-seq: clamp(local_end - qs_b, 0, len_b);
- *                                     round-robin: last local position + 1, or 0)
+ *                                    (in-seq: P_b + clamp(local_end - qs_b, 0, n_b);
+ *                                     round-robin: P_b + last local position + 1, or P_b)
  *   local_kv_start_loc    [batch+1]  KV row where request b starts (in-seq: right-aligned
- *                                    cumsum of local_seq_lens; round-robin: query_start_loc)
+ *                                    cumsum of local_seq_lens; round-robin: the segment
+ *                                    starts, = query_start_loc in pure prefill)
  *   scalars [8]: num_tokens_pad, tokens_per_rank, local_start, local_end, stride (1 or cp),
  *                n_local_real, max_seqlen_q, num_local_reqs
  *   token_map [tokens_per_rank] (optional): global token id of each local row, -1 for pads
- *   err_flag [1] (optional): DSA_DEVERR_QSL_* / DSA_DEVERR_NOT_PREFILL bits
+ *   err_flag [1] (optional): DSA_DEVERR_QSL_* / DSA_DEVERR_SEQ_LENS bits (a request flagged
+ *                            SEQ_LENS is treated as having no prefix)
  * Local query j (0-based) of request b, with n_b = local_query_start_loc[b+1] - [b], sees the
  * keys [local_kv_start_loc[b], local_kv_start_loc[b] + E) with
  *   E = local_seq_lens[b] - (n_b - 1 - j) * stride.

@@ -15,11 +15,13 @@ Pages cited (by title and section):
 Readings of points the pages leave open are tagged R-n; they are listed with their reasons
 in the design notes of this repository:
   R-1  in-seq local_start/local_end clamp to T; trailing ranks may hold only pad rows.
-  R-2  every request keeps its entry; in-seq local_seq_lens[b] = clamp(local_end - qs_b, 0, len_b).
+  R-2  every request keeps its entry; in-seq local_seq_lens[b] = P_b + clamp(local_end - qs_b, 0, len_b)
+       (P_b = the cached prefix of R-17, 0 in pure prefill).
   R-3  multi-request in-seq split cuts the flattened stream.
   R-4  round-robin padding appends pad rows at the end of the flattened stream.
-  R-5  round-robin local_seq_lens = extent of the request's last local query;
-       local_kv_start_loc = the global query_start_loc; per-query extents step by cp.
+  R-5  round-robin local_seq_lens = extent of the request's last local query (P_b without one);
+       local_kv_start_loc = where each request's KV segment starts (the global query_start_loc
+       in pure prefill); per-query extents step by cp.
   R-6  a query sees itself (position p sees keys 0..p).
   R-7  one indexer key per token, shared by all indexer heads; weights per (token, head).
   R-8  fp8: q_hat = q8 * q_scale[token, head], k_hat = k8 * k_scale[token], scales > 0.
@@ -29,7 +31,10 @@ in the design notes of this repository:
   R-12 compressed indexer: attend the selected compressed rows plus the window's original rows.
   R-13 window = the last `window` positions up to and including the query.
   R-16 unpadded round-robin rerange: rank r's rows start at sum_{r'<r} ceil((T - r')/cp).
-  R-17 seq_lens must equal the query lengths (pure prefill); anything else is rejected.
+  R-17 seq_lens[b] >= the query length n_b; the difference P_b is a cached prefix (chunked
+       prefill).  Request b's KV segment holds seq_lens[b] rows, prefix first, and the
+       segments follow one another in request order; query g (0-based) of the request sits at
+       KV position P_b + g.  Pure prefill is P_b = 0.
   R-18 local rows are ordered by global token index; pad rows come last.
 """
 import numpy as np
@@ -86,16 +91,21 @@ def decode(x, dtype):
 #   Part 3.1 (per-rank counts differ by at most one).
 # ---------------------------------------------------------------------------------------------
 
-def check_prefill_lengths(qsl, seq_lens):
+def check_lengths(qsl, seq_lens):
     qsl = np.asarray(qsl, dtype=np.int64)
     seq_lens = np.asarray(seq_lens, dtype=np.int64)
     if qsl.ndim != 1 or len(qsl) != len(seq_lens) + 1 or qsl[0] != 0:
         raise ValueError("query_start_loc must be [B+1] starting at 0")
     if np.any(np.diff(qsl) < 0):
         raise ValueError("query_start_loc must be non-decreasing")
-    if np.any(np.diff(qsl) != seq_lens):                      # R-17
-        raise ValueError("seq_lens must equal the query lengths (pure prefill)")
+    if np.any(seq_lens < np.diff(qsl)):                       # R-17
+        raise ValueError("seq_lens must be at least the query lengths")
     return qsl, seq_lens
+
+
+def kv_start_loc(seq_lens):
+    """Row where each request's KV segment starts in the full stream (R-17): [B+1]."""
+    return np.concatenate([[0], np.cumsum(np.asarray(seq_lens, dtype=np.int64))])
 
 
 def local_tokens(T, cp_size, cp_rank, mode):
@@ -119,7 +129,7 @@ def cp_metadata(qsl, seq_lens, cp_size, cp_rank, mode, pad_to_cp):
       local_query_start_loc [B+1], local_seq_lens [B], local_kv_start_loc [B+1],
       token_map [tokens_per_rank] (global token id of each local row, -1 for pad rows).
     """
-    qsl, seq_lens = check_prefill_lengths(qsl, seq_lens)
+    qsl, seq_lens = check_lengths(qsl, seq_lens)
     if not (0 <= cp_rank < cp_size):
         raise ValueError("need 0 <= cp_rank < cp_size")
     B = len(seq_lens)
@@ -140,17 +150,18 @@ def cp_metadata(qsl, seq_lens, cp_size, cp_rank, mode, pad_to_cp):
     lsl = np.zeros(B, dtype=np.int64)
     for b in range(B):
         qs, qe = int(qsl[b]), int(qsl[b + 1])
+        prefix = int(seq_lens[b]) - (qe - qs)                        # R-17
         mine = toks[(toks >= qs) & (toks < qe)]
         n_b[b] = len(mine)
-        if mode == IN_SEQ:
-            lsl[b] = min(max(local_end - qs, 0), qe - qs)           # R-2
-        else:
-            lsl[b] = (int(mine[-1]) - qs + 1) if len(mine) else 0    # R-5
+        if mode == IN_SEQ:                                           # R-2
+            lsl[b] = prefix + min(max(local_end - qs, 0), qe - qs)
+        else:                                                        # R-5
+            lsl[b] = prefix + ((int(mine[-1]) - qs + 1) if len(mine) else 0)
     lqsl = np.concatenate([[0], np.cumsum(n_b)])
     if mode == IN_SEQ:
         lkv = np.concatenate([[0], np.cumsum(lsl)])                  # right-aligned cumsum
     else:
-        lkv = qsl.copy()                                             # R-5
+        lkv = kv_start_loc(seq_lens)                                 # R-5
     token_map = np.full(tpr, -1, dtype=np.int64)
     token_map[:len(toks)] = toks                                     # R-18: pads last
     # Unpadded round-robin: rows past the rank's real tokens are not rows at all; the map still
@@ -334,8 +345,10 @@ def dense_causal_attention(q, kv, sink, scale, Dv):
 def run_path(meta, inputs, wl, rows=None, scale=None, want_scores=False):
     """Indexer -> top-k (+window) -> sparse attention for local rows `rows` (default: all).
 
-    inputs: dict of stored arrays (q, q_idx, w, q_scale?, kv, k_idx, k_scale?, sink,
+    inputs: dict of stored arrays (q, q_idx, w, q_scale?, kv, k_idx, k_scale?, sink, seq_lens,
             kv_cmp_start? for compressed keys); q/q_idx/w/q_scale indexed by local row.
+            kv holds the token rows of every request's KV segment (R-17), then, with
+            compressed keys, the compressed rows.
     Returns dict with per-row lists: topk_ids (absolute KV rows, ascending), window_ids,
     out [n, H, D_v] float64, lse [n, H], and optionally the float64 score rows.
     """
@@ -347,8 +360,8 @@ def run_path(meta, inputs, wl, rows=None, scale=None, want_scores=False):
     kv = decode(inputs["kv"], wl.attn_dtype)
     k_hat = dequant_k(inputs["k_idx"], inputs.get("k_scale"), wl.idx_dtype)
     sink = np.asarray(inputs["sink"], dtype=np.float32).astype(np.float64)
-    qsl = np.asarray(inputs["qsl"], dtype=np.int64)
-    T = int(qsl[-1])
+    kvsl = kv_start_loc(inputs["seq_lens"])                   # R-17: request b's KV segment
+    n_kv = int(kvsl[-1])
     res = dict(topk_ids=[], window_ids=[], out=np.zeros((len(rows), wl.H, wl.Dv)),
                lse=np.zeros((len(rows), wl.H)), scores=[])
     for n, i in enumerate(rows):
@@ -360,12 +373,12 @@ def run_path(meta, inputs, wl, rows=None, scale=None, want_scores=False):
             nvis = visible_keys(E, wl.compress)
             krows = k_hat[c0:c0 + nvis]
             sc = indexer_scores_row(q_hat, inputs["w"][i], krows)
-            ids = T + c0 + topk_positions(sc, wl.topk)    # compressed rows follow the T rows
+            ids = n_kv + c0 + topk_positions(sc, wl.topk)  # compressed rows follow the token rows
         else:
             krows = k_hat[kv0:kv0 + E]
             sc = indexer_scores_row(q_hat, inputs["w"][i], krows)
             ids = kv0 + topk_positions(sc, wl.topk)
-        win = (int(qsl[b]) + window_positions(E, wl.window)) if wl.window else np.zeros(0, np.int64)
+        win = (int(kvsl[b]) + window_positions(E, wl.window)) if wl.window else np.zeros(0, np.int64)
         res["topk_ids"].append(ids)
         res["window_ids"].append(win)
         if want_scores:

@@ -7,6 +7,10 @@
 // [CP-blog] "[DeepSeek v3.2] context parallel explained", §2B (round-robin split by
 // token % cp_size and recomputed per-rank cu-seqlens).
 //
+// Chunked prefill: request b may carry P_b = seq_lens[b] - n_b cached tokens ahead of its
+// n_b queries; its KV segment (seq_lens[b] rows, prefix first) follows the previous request's,
+// and every extent counts the prefix.
+//
 // One workgroup of 1024 threads computes every per-request value with closed forms (no loop
 // over tokens) and wavefront prefix scans; all workgroups fill the token map.
 #include "dsa_internal.h"
@@ -83,48 +87,56 @@ __global__ __launch_bounds__(kThreads) void cp_metadata_kernel(
   }
   __syncthreads();
 
-  int carry_q = 0, carry_kv = 0;
+  int carry_q = 0, carry_kv = 0, carry_seg = 0;
   int bad = 0;
   for (int base = 0; base < batch; base += kThreads) {
     const int b = base + threadIdx.x;
-    int nb = 0, ext = 0, qs = 0;
+    int nb = 0, ext = 0, seg = 0;
     if (b < batch) {
-      qs = qsl[b];
+      const int qs = qsl[b];
       const int qe = qsl[b + 1];
       if (b == 0 && qs != 0) bad |= DSA_DEVERR_QSL_START;
       if (qe < qs) bad |= DSA_DEVERR_QSL_ORDER;
-      if (seq_lens[b] != qe - qs) bad |= DSA_DEVERR_NOT_PREFILL;
       if (b == batch - 1 && qe != T) bad |= DSA_DEVERR_QSL_TOTAL;
       const int len = max(qe - qs, 0);
+      int prefix = seq_lens[b] - len;
+      if (prefix < 0) {
+        bad |= DSA_DEVERR_SEQ_LENS;
+        prefix = 0;
+      }
+      seg = prefix + len;
       if (rr) {
         nb = max(rr_count_below(qe, cp, rank) - rr_count_below(qs, cp, rank), 0);
+        ext = prefix;
         if (nb > 0) {
           const int t_last = rank + (rr_count_below(qe, cp, rank) - 1) * cp;
-          ext = t_last - qs + 1;
+          ext += t_last - qs + 1;
         }
       } else {
         nb = max(min(qe, local_end) - max(qs, local_start), 0);
-        ext = min(max(local_end - qs, 0), len);
+        ext = prefix + min(max(local_end - qs, 0), len);
       }
       lsl[b] = ext;
       atomicMax(&s_max, nb);
       if (nb > 0) atomicAdd(&s_nreq, 1);
     }
-    int tot_q, tot_kv;
+    int tot_q, tot_kv, tot_seg;
     const int ex_q = block_excl_scan(nb, smem, &tot_q);
     const int ex_kv = block_excl_scan(ext, smem, &tot_kv);
+    const int ex_seg = block_excl_scan(seg, smem, &tot_seg);
     if (b < batch) {
       lqsl[b] = carry_q + ex_q;
-      lkv[b] = rr ? qs : carry_kv + ex_kv;
+      lkv[b] = rr ? carry_seg + ex_seg : carry_kv + ex_kv;
     }
     carry_q += tot_q;
     carry_kv += tot_kv;
+    carry_seg += tot_seg;
   }
   if (bad) raise_flag(err_flag, bad);
   __syncthreads();
   if (threadIdx.x == 0) {
     lqsl[batch] = carry_q;
-    lkv[batch] = rr ? (batch > 0 ? qsl[batch] : 0) : carry_kv;
+    lkv[batch] = rr ? carry_seg : carry_kv;
     scalars[0] = tpr * cp;
     scalars[1] = tpr;
     scalars[2] = local_start;

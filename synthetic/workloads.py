@@ -8,9 +8,14 @@ Recipe (every workload): values are drawn in float64 from numpy's PCG64, seeded 
 SeedSequence([workload_id, tensor_id, block]) and rounded once (RNE) to the storage dtype.
   q, kv         ~ N(0,1)/sqrt(D_qk)        q_idx, k_idx ~ N(0,1)/sqrt(D_i)
   w             ~ N(0,1)/sqrt(H_i)         sink         ~ N(0,1)
-Per-query tensors (q, q_idx, w, q_scale) are seeded per token, so any rank's rows can be
-drawn alone and every rank sees the same value for the same token.  Full-stream tensors
-(kv, k_idx, k_scale) are seeded per block of 64 tokens.
+Per-query tensors (q, q_idx, w, q_scale) are seeded per token, by the KV-stream row the token
+occupies, so any rank's rows can be drawn alone, every rank sees the same value for the same
+token, and a chunk of a request carries the same values as that part of the whole request.
+Full-stream tensors (kv, k_idx, k_scale) are seeded per block of 64 KV rows.
+
+Chunked prefill: request b may carry a cached prefix of prefix[b] tokens.  Its KV segment
+then holds prefix[b] + lens[b] rows (prefix first) and the segments follow one another in
+request order; the queries are the lens[b] new tokens only.
 
 Variants: "normal" (above), "unit" (q, kv, q_idx, k_idx ~ N(0,1): logits of order one) and
 "int" (q_idx, k_idx integers in [-4,4], w integers in [-2,2], fp8 scales powers of two, so
@@ -29,7 +34,7 @@ STREAM_BLOCK = 64
 class Workload:
     name: str
     wid: int                 # seed id
-    lens: tuple              # request lengths (prefill: query length == KV length)
+    lens: tuple              # query tokens per request (the new tokens)
     cp: int
     rank: int
     mode: str                # "in_seq" | "round_robin"
@@ -46,6 +51,7 @@ class Workload:
     compress: int = 1        # indexer runs over keys compressed by this ratio
     rerange: bool = False    # also permute a rank-concatenated [T, D_qk] buffer
     notes: str = ""
+    prefix: tuple = ()       # cached tokens before each request's queries (empty: none)
 
     @property
     def T(self):
@@ -54,6 +60,21 @@ class Workload:
     @property
     def qsl(self):
         return np.concatenate([[0], np.cumsum(np.asarray(self.lens, dtype=np.int64))]).astype(np.int32)
+
+    @property
+    def seq_lens(self):
+        """KV tokens per request: cached prefix plus the new tokens."""
+        p = self.prefix or (0,) * len(self.lens)
+        return (np.asarray(self.lens, dtype=np.int64) + np.asarray(p, dtype=np.int64)).astype(np.int32)
+
+    @property
+    def kvsl(self):
+        """Start row of each request's KV segment, [B+1]."""
+        return np.concatenate([[0], np.cumsum(self.seq_lens.astype(np.int64))]).astype(np.int32)
+
+    @property
+    def n_kv(self):
+        return int(self.seq_lens.astype(np.int64).sum())
 
     @property
     def k_tot(self):
@@ -84,6 +105,11 @@ WORKLOADS = {
     "long_131k_fp8": Workload(
         "long_131k_fp8", 4, (131072,), 8, 7, "in_seq", False, 128, 576, 512, "bf16", 64, 128, "fp8", 2048,
         notes="131072 tokens, contiguous cp 8 last rank (16384 queries); fp8 e4m3 indexer"),
+    "chunk_inseq_cp8_last_8k_p56k": Workload(
+        "chunk_inseq_cp8_last_8k_p56k", 6, (8192,), 8, 7, "in_seq", False, 128, 576, 512, "bf16", 64, 128,
+        "bf16", 2048, prefix=(57344,),
+        notes="chunked prefill: an 8192-token chunk after a 57344-token cached prefix, contiguous cp 8, "
+              "last rank: 1024 queries over up to 65536 KV"),
     "rr_cp4_r1_var8_cmp4": Workload(
         "rr_cp4_r1_var8_cmp4", 5, _var_lens(), 4, 1, "round_robin", True, 128, 576, 512, "bf16", 64, 128,
         "bf16", 2048, window=128, compress=4,
@@ -143,22 +169,25 @@ class _WL:
         self._variant = variant
         self.T = wl.T
         self.qsl = wl.qsl
+        self.seq_lens = wl.seq_lens
+        self.kvsl = wl.kvsl
+        self.n_kv = wl.n_kv
 
 
 def stream_inputs(wl: Workload, variant="normal"):
     """Full-stream tensors: kv rows, indexer keys (+ fp8 scales), sink; compressed stand-ins.
 
-    Returns a dict of numpy arrays in storage dtype:
-      kv      [T + Tc, D_qk]  (Tc compressed latent rows follow the T token rows when compress > 1)
-      k_idx   [T or Tc, D_i]  (compressed keys only when compress > 1)
-      k_scale [T] float32     (fp8 only)
+    Returns a dict of numpy arrays in storage dtype (N = n_kv KV rows, = T without prefixes):
+      kv      [N + Nc, D_qk]  (Nc compressed latent rows follow the N token rows when compress > 1)
+      k_idx   [N or Nc, D_i]  (compressed keys only when compress > 1)
+      k_scale [N] float32     (fp8 only)
       sink    [H] float32
       kv_cmp_start [B+1] int32 (compress > 1: offset of request b's compressed rows)
     """
     w = _WL(wl, variant)
-    T = wl.T
+    T = wl.n_kv
     unit = variant == "unit"
-    out = {"qsl": wl.qsl, "seq_lens": np.asarray(wl.lens, dtype=np.int32)}
+    out = {"qsl": wl.qsl, "seq_lens": wl.seq_lens}
     kv = _stream_rows(w, T_KV, T, wl.Dqk, _normal(1.0 if unit else 1.0 / np.sqrt(wl.Dqk)))
     if variant == "int":
         kidx = _stream_rows(w, T_KIDX, T, wl.Di, _ints(-4, 4))
@@ -179,16 +208,16 @@ def stream_inputs(wl: Workload, variant="normal"):
 
     if wl.compress > 1:
         # Compressor stand-in: mean of each non-overlapping block of `compress` tokens of a
-        # request (trailing partial block dropped), computed in float64 from the stored values
-        # and rounded once.  The pages name a compressor but do not define it.
+        # request's KV segment (trailing partial block dropped), computed in float64 from the
+        # stored values and rounded once.  The pages name a compressor but do not define it.
         r = wl.compress
-        qsl = wl.qsl
-        nblk = [l // r for l in wl.lens]
+        kvsl = wl.kvsl
+        nblk = [int(l) // r for l in wl.seq_lens]
         kv_dec = kv_st.astype(np.float64) if wl.attn_dtype == "f32" else bf16_bits_to_f64(kv_st)
         kidx_dec = out["k_idx"].astype(np.float64) if wl.idx_dtype == "f32" else bf16_bits_to_f64(out["k_idx"])
         kv_c, ki_c = [], []
-        for b, l in enumerate(wl.lens):
-            s = int(qsl[b])
+        for b in range(len(wl.lens)):
+            s = int(kvsl[b])
             n = nblk[b]
             kv_c.append(kv_dec[s:s + n * r].reshape(n, r, wl.Dqk).mean(axis=1))
             ki_c.append(kidx_dec[s:s + n * r].reshape(n, r, wl.Di).mean(axis=1))
@@ -205,10 +234,15 @@ def query_inputs(wl: Workload, tokens, variant="normal"):
     """Per-query tensors for the given global token ids (pads: id < 0 give zero rows).
 
     Returns q [n,H,D_qk], q_idx [n,H_i,D_i], w [n,H_i] float32, and q_scale [n,H_i] for fp8,
-    filled token by token straight into the storage dtype.
+    filled token by token straight into the storage dtype.  Token t of request b is seeded by
+    its KV row kvsl[b] + prefix[b] + (t - qsl[b]) (= t without prefixes).
     """
     tokens = np.asarray(tokens, dtype=np.int64)
     n = len(tokens)
+    qsl = wl.qsl.astype(np.int64)
+    req = np.clip(np.searchsorted(qsl, tokens, side="right") - 1, 0, max(len(wl.lens) - 1, 0))
+    kv_row = (wl.kvsl.astype(np.int64)[req] + (wl.seq_lens.astype(np.int64) - np.diff(qsl))[req]
+              + tokens - qsl[req]) if len(wl.lens) else tokens
     unit = variant == "unit"
     sq = 1.0 if unit else 1.0 / np.sqrt(wl.Dqk)
     si = 1.0 if unit else 1.0 / np.sqrt(wl.Di)
@@ -220,9 +254,10 @@ def query_inputs(wl: Workload, tokens, variant="normal"):
     for j, t in enumerate(tokens):
         if t < 0:
             continue
-        g = _rng(wl.wid, T_Q, t, variant)
+        row = int(kv_row[j])
+        g = _rng(wl.wid, T_Q, row, variant)
         q[j] = _store(g.standard_normal((wl.H, wl.Dqk)) * sq, wl.attn_dtype)
-        g = _rng(wl.wid, T_QIDX, t, variant)
+        g = _rng(wl.wid, T_QIDX, row, variant)
         if variant == "int":
             x = g.integers(-4, 5, size=(wl.Hi, wl.Di)).astype(np.float64)
             w[j] = g.integers(-2, 3, size=wl.Hi)

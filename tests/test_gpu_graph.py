@@ -17,7 +17,7 @@ def test_graph_replays_equal_eager(name, kw):
     import sparse_attention_prefill_amd as D
     wl = S.WORKLOADS[name].with_(**kw)
     mode = 0 if wl.mode == "in_seq" else 1
-    qsl_d, lens_d = to_dev(wl.qsl, "i32", dev), to_dev(np.asarray(wl.lens), "i32", dev)
+    qsl_d, lens_d = to_dev(wl.qsl, "i32", dev), to_dev(wl.seq_lens, "i32", dev)
     _, n_real, _ = D.cp_sizes(wl.T, wl.cp, wl.rank, mode, wl.pad)
     meta0 = D.build_cp_metadata(qsl_d, lens_d, wl.T, wl.cp, wl.rank, mode, wl.pad)
     torch.cuda.synchronize()
@@ -30,16 +30,16 @@ def test_graph_replays_equal_eager(name, kw):
     out = torch.empty(n_real, wl.H, wl.Dv, dtype=torch.bfloat16, device=dev)
     ws = torch.empty(D.indexer_topk_workspace(qi, w, ki, meta0["local_query_start_loc"], meta0["local_seq_lens"],
                                               kv_cmp if kv_cmp is not None else meta0["local_kv_start_loc"],
-                                              max(wl.lens), topk=wl.topk, window=wl.window,
+                                              int(wl.seq_lens.max()), topk=wl.topk, window=wl.window,
                                               window_kv_start=meta0["local_kv_start_loc"],
                                               compress_ratio=wl.compress), dtype=torch.uint8, device=dev)
 
     def step():
         m = D.build_cp_metadata(qsl_d, lens_d, wl.T, wl.cp, wl.rank, mode, wl.pad)
         D.indexer_topk(qi, w, ki, m["local_query_start_loc"], m["local_seq_lens"],
-                       kv_cmp if kv_cmp is not None else m["local_kv_start_loc"], max(wl.lens), topk_idx=idx,
+                       kv_cmp if kv_cmp is not None else m["local_kv_start_loc"], int(wl.seq_lens.max()), topk_idx=idx,
                        workspace=ws, topk=wl.topk, q_stride=wl.cp if mode else 1, compress_ratio=wl.compress,
-                       kv_row_base=wl.T if wl.compress > 1 else 0, window=wl.window,
+                       kv_row_base=wl.n_kv if wl.compress > 1 else 0, window=wl.window,
                        window_kv_start=m["local_kv_start_loc"] if wl.window else None)
         D.sparse_attn(q, kv, idx, sink, 1.0 / np.sqrt(wl.Dqk), wl.Dv, out=out)
 

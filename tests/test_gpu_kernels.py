@@ -92,7 +92,7 @@ def test_topk_compressed_and_window():
 
 def _indexer_case(wl, variant, dev, rows_cap=None):
     import sparse_attention_prefill_amd as D
-    m = O.cp_metadata(wl.qsl, wl.lens, wl.cp, wl.rank, wl.mode, wl.pad)
+    m = O.cp_metadata(wl.qsl, wl.seq_lens, wl.cp, wl.rank, wl.mode, wl.pad)
     toks = m["token_map"][m["token_map"] >= 0]
     inp = S.stream_inputs(wl, variant)
     qin = S.query_inputs(wl, toks, variant)
@@ -147,6 +147,10 @@ def _indexer_case(wl, variant, dev, rows_cap=None):
     # any single range and ends just past a multiple of the 2048-key chunk
     ("inseq_cp8_last_8k", {"lens": (2046, 3), "cp": 2, "rank": 1}),
     ("long_131k_fp8", {"lens": (2045, 50), "cp": 8, "rank": 7}),
+    # chunked prefill: queries start deep into their request's KV segment
+    ("chunk_inseq_cp8_last_8k_p56k", {"lens": (1500,), "prefix": (3333,), "cp": 2, "rank": 0}),
+    ("rr_cp8_r3_batch4", {"lens": (700, 130, 5), "prefix": (2500, 1, 90)}),
+    ("long_131k_fp8", {"lens": (1000, 9), "prefix": (5000, 4100), "cp": 2, "rank": 1}),
 ])
 def test_indexer_scores(name, kw, variant):
     dev = gpu()

@@ -27,21 +27,27 @@ def _batches():
 
 
 @pytest.mark.parametrize("mode", [O.IN_SEQ, O.ROUND_ROBIN])
-def test_metadata_matches_oracle(mode):
+@pytest.mark.parametrize("prefixed", [False, True])
+def test_metadata_matches_oracle(mode, prefixed):
+    """prefixed: every request also carries a random cached prefix (chunked prefill)."""
     dev = gpu()
     import sparse_attention_prefill_amd as D
+    g = np.random.default_rng(101)
     for lens in _batches():
         qsl = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
         T = int(qsl[-1])
+        seq = np.asarray(lens, dtype=np.int64)
+        if prefixed:
+            seq = seq + g.integers(0, 5000, size=len(lens))
         for cp in (1, 2, 3, 4, 8):
             for pad in (False, True):
                 for r in sorted({0, cp // 2, cp - 1}):
-                    ref = O.cp_metadata(qsl, lens, cp, r, mode, pad)
+                    ref = O.cp_metadata(qsl, seq, cp, r, mode, pad)
                     err = torch.zeros(1, dtype=torch.int32, device=dev)
-                    m = D.build_cp_metadata(to_dev(qsl, "i32", dev), to_dev(np.array(lens), "i32", dev), T, cp, r,
+                    m = D.build_cp_metadata(to_dev(qsl, "i32", dev), to_dev(seq, "i32", dev), T, cp, r,
                                             mode_code(mode), pad, err_flag=err)
                     torch.cuda.synchronize()
-                    tag = f"lens={lens[:6]}.. cp={cp} r={r} pad={pad}"
+                    tag = f"lens={lens[:6]}.. seq={list(seq[:6])}.. cp={cp} r={r} pad={pad}"
                     assert err.item() == 0, tag
                     for k in ("local_query_start_loc", "local_seq_lens", "local_kv_start_loc", "token_map"):
                         assert np.array_equal(m[k].cpu().numpy(), ref[k]), f"{k} {tag}"
@@ -55,7 +61,7 @@ def test_metadata_flags_bad_inputs():
     dev = gpu()
     import sparse_attention_prefill_amd as D
     qsl = to_dev(np.array([0, 4, 9]), "i32", dev)
-    for seq, T, bit in (([4, 6], 9, 0x4), ([4, 5], 10, 0x8)):
+    for seq, T, bit in (([4, 3], 9, 0x4), ([3, 5], 9, 0x4), ([4, 5], 10, 0x8)):
         err = torch.zeros(1, dtype=torch.int32, device=dev)
         D.build_cp_metadata(qsl, to_dev(np.array(seq), "i32", dev), T, 2, 0, 0, False, err_flag=err)
         torch.cuda.synchronize()

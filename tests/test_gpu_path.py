@@ -23,7 +23,7 @@ def gpu_rank_path(wl, variant, dev, rank=None, keep_scores=False):
     mode = 0 if wl.mode == O.IN_SEQ else 1
     inp = S.stream_inputs(wl, variant)
     qsl_d = to_dev(wl.qsl, "i32", dev)
-    lens_d = to_dev(np.asarray(wl.lens), "i32", dev)
+    lens_d = to_dev(wl.seq_lens, "i32", dev)
     err = torch.zeros(1, dtype=torch.int32, device=dev)
     meta = D.build_cp_metadata(qsl_d, lens_d, wl.T, wl.cp, rank, mode, wl.pad, err_flag=err)
     torch.cuda.synchronize()
@@ -31,11 +31,11 @@ def gpu_rank_path(wl, variant, dev, rank=None, keep_scores=False):
     toks = meta["token_map"].cpu().numpy()[:n_real]
     qin = S.query_inputs(wl, toks, variant)
     ik = wl.idx_dtype
-    max_kv = max(wl.lens)
+    max_kv = int(wl.seq_lens.max())
     cu_kv = to_dev(inp["kv_cmp_start"], "i32", dev) if wl.compress > 1 else meta["local_kv_start_loc"]
     q_idx = to_dev(qin["q_idx"], ik, dev)
     kw = dict(topk=wl.topk, q_stride=int(meta["scalars"][4].item()), compress_ratio=wl.compress,
-              kv_row_base=wl.T if wl.compress > 1 else 0, window=wl.window,
+              kv_row_base=wl.n_kv if wl.compress > 1 else 0, window=wl.window,
               window_kv_start=meta["local_kv_start_loc"] if wl.window else None,
               q_scale=to_dev(qin["q_scale"], "f32", dev) if "q_scale" in qin else None,
               k_scale=to_dev(inp["k_scale"], "f32", dev) if "k_scale" in inp else None, err_flag=err)
@@ -58,7 +58,7 @@ def gpu_rank_path(wl, variant, dev, rank=None, keep_scores=False):
 
 
 def check_against_oracle(wl, variant, res, rows=None, min_same=0.99):
-    m = O.cp_metadata(wl.qsl, wl.lens, wl.cp, wl.rank, wl.mode, wl.pad)
+    m = O.cp_metadata(wl.qsl, wl.seq_lens, wl.cp, wl.rank, wl.mode, wl.pad)
     assert res["err"] == 0
     for k in ("local_query_start_loc", "local_seq_lens", "local_kv_start_loc", "token_map"):
         assert np.array_equal(res["meta"][k], m[k]), k
@@ -67,7 +67,7 @@ def check_against_oracle(wl, variant, res, rows=None, min_same=0.99):
     ora = O.run_path(m, {**res["inp"], **{k: v for k, v in res["qin"].items()}}, wl, rows=rows, want_scores=True)
     K = wl.topk
     views = O.query_views(m)
-    base = [((wl.T + res["inp"]["kv_cmp_start"][views[i][0]]) if wl.compress > 1 else views[i][2]) for i in rows]
+    base = [((wl.n_kv + res["inp"]["kv_cmp_start"][views[i][0]]) if wl.compress > 1 else views[i][2]) for i in rows]
     gpu_topk = [res["idx"][i, :K] for i in rows]
     if variant == "int":
         for n_, i in enumerate(rows):
@@ -118,7 +118,8 @@ def test_path_integer_inputs_topk_exact(name, kw):
     check_against_oracle(wl, "int", res, rows=rows)
 
 
-@pytest.mark.parametrize("name", ["inseq_cp8_last_8k", "rr_cp8_r3_batch4", "rr_cp4_r1_var8_cmp4", "long_131k_fp8"])
+@pytest.mark.parametrize("name", ["inseq_cp8_last_8k", "rr_cp8_r3_batch4", "rr_cp4_r1_var8_cmp4", "long_131k_fp8",
+                                  "chunk_inseq_cp8_last_8k_p56k"])
 def test_path_full_size_sampled(name):
     dev = gpu()
     wl = S.WORKLOADS[name]
@@ -164,3 +165,57 @@ def test_path_is_deterministic():
     b = gpu_rank_path(wl, "normal", dev)
     assert np.array_equal(a["idx"], b["idx"])
     assert torch.equal(a["out"].view(torch.int16), b["out"].view(torch.int16))
+
+
+# Chunked prefill: every request carries a cached prefix ahead of its queries (its KV segment is
+# prefix + queries long).  Reduced sizes that still span several tiles and a ragged tail.
+CHUNKED = [
+    ("chunk_inseq_cp8_last_8k_p56k", {"lens": (2048,), "prefix": (6000,)}),
+    ("rr_cp8_r3_batch4", {"lens": (1500, 700, 130, 5), "prefix": (3000, 0, 517, 20)}),
+    ("long_131k_fp8", {"lens": (2048,), "prefix": (9001,)}),
+    ("rr_cp4_r1_var8_cmp4", {"lens": (1000, 2001, 300), "prefix": (4000, 3, 0)}),
+]
+
+
+@pytest.mark.parametrize("name,kw", CHUNKED)
+def test_chunked_prefill_every_row(name, kw):
+    dev = gpu()
+    wl = S.WORKLOADS[name].with_(**kw)
+    res = gpu_rank_path(wl, "normal", dev)
+    n = res["n_real"]
+    rows = range(n) if n <= 160 else np.unique(np.linspace(0, n - 1, 160).astype(int))
+    # Rows of 10k+ fp8-scored keys put more near-equal scores at the cut: every differing id is
+    # still checked against the tie band, only the floor on identical sets is lower.
+    check_against_oracle(wl, "normal", res, rows=rows, min_same=0.95 if wl.idx_dtype == "fp8" else 0.99)
+
+
+@pytest.mark.parametrize("name,kw", CHUNKED)
+def test_chunked_prefill_integer_inputs_topk_exact(name, kw):
+    dev = gpu()
+    wl = S.WORKLOADS[name].with_(**kw)
+    res = gpu_rank_path(wl, "int", dev)
+    n = res["n_real"]
+    rows = range(n) if n <= 100 else np.unique(np.linspace(0, n - 1, 100).astype(int))
+    check_against_oracle(wl, "int", res, rows=rows)
+
+
+@pytest.mark.parametrize("mode,cp,rank,pad", [(O.IN_SEQ, 4, 3, False), (O.ROUND_ROBIN, 3, 1, True)])
+def test_chunked_prefill_equals_the_whole_requests_bitwise(mode, cp, rank, pad):
+    """The last chunks of two requests, run after their cached prefixes on one rank, give the
+    same top-k rows and the same output bits as the whole requests run at cp 1."""
+    dev = gpu()
+    whole = S.WORKLOADS["inseq_cp8_last_8k"].with_(lens=(3000, 1100), cp=1, rank=0, mode=O.IN_SEQ, pad=False,
+                                                    topk=512)
+    full = gpu_rank_path(whole, "normal", dev)
+    prefix = (1900, 37)
+    chunk = whole.with_(lens=(1100, 1063), prefix=prefix, cp=cp, rank=rank, mode=mode, pad=pad)
+    assert list(chunk.seq_lens) == list(whole.lens)
+    res = gpu_rank_path(chunk, "normal", dev)
+    assert res["err"] == 0
+    toks = res["toks"]
+    b = np.searchsorted(chunk.qsl, toks, side="right") - 1
+    whole_rows = whole.qsl[b] + np.asarray(prefix)[b] + toks - chunk.qsl[b]
+    assert np.array_equal(res["idx"], full["idx"][whole_rows])
+    got = res["out"].view(torch.int16).cpu().numpy()
+    want = full["out"].view(torch.int16).cpu().numpy()[whole_rows]
+    assert np.array_equal(got, want)

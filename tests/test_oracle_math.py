@@ -283,3 +283,60 @@ def test_selected_rows_are_causal_and_absolute():
         b = np.searchsorted(wl.qsl, t, side="right") - 1
         assert len(ids) == min(4, t - wl.qsl[b] + 1)
         assert np.all((ids >= wl.qsl[b]) & (ids <= t))
+
+
+@pytest.mark.parametrize("mode,cp,rank,pad,compress,window", [
+    (O.IN_SEQ, 1, 0, False, 1, 0), (O.IN_SEQ, 3, 2, False, 1, 0), (O.ROUND_ROBIN, 3, 1, False, 1, 0),
+    (O.ROUND_ROBIN, 2, 1, True, 4, 5), (O.IN_SEQ, 2, 1, True, 4, 5)])
+def test_chunked_prefill_equals_the_rows_of_the_whole_requests(mode, cp, rank, pad, compress, window):
+    """R-17: the last chunk of each request, run after its cached prefix, gives exactly the rows
+    the whole requests give at the same KV positions (same keys, same top-k, same output).
+
+    The whole run is cp 1 pure prefill, whose rows are pinned above; a wrong prefix offset,
+    extent or KV segment start in the chunked metadata changes the keys a row sees.
+    """
+    whole = _tiny_wl(O.IN_SEQ, 1, 0, False, lens=(13, 7, 22), topk=4, compress=compress, window=window)
+    m1 = O.cp_metadata(whole.qsl, whole.seq_lens, 1, 0, O.IN_SEQ, False)
+    inp = S.stream_inputs(whole)
+    full = O.run_path(m1, {**inp, **S.query_inputs(whole, m1["token_map"])}, whole, want_scores=True)
+    prefix = (9, 0, 17)
+    chunk = whole.with_(lens=tuple(l - p for l, p in zip(whole.lens, prefix)), prefix=prefix,
+                        mode=mode, cp=cp, rank=rank, pad=pad)
+    assert list(chunk.seq_lens) == list(whole.lens)
+    cinp = S.stream_inputs(chunk)
+    for k in ("kv", "k_idx", "kv_cmp_start"):
+        if k in inp:
+            assert np.array_equal(cinp[k], inp[k]), k
+    m = O.cp_metadata(chunk.qsl, chunk.seq_lens, cp, rank, mode, pad)
+    toks = m["token_map"][m["token_map"] >= 0]
+    assert len(toks) > 0
+    res = O.run_path(m, {**cinp, **S.query_inputs(chunk, m["token_map"])}, chunk, want_scores=True)
+    for n, t in enumerate(toks):
+        b = int(np.searchsorted(chunk.qsl, t, side="right") - 1)
+        row = int(whole.qsl[b]) + prefix[b] + int(t - chunk.qsl[b])    # KV row = whole-run row
+        assert np.array_equal(res["scores"][n], full["scores"][row])
+        assert np.array_equal(res["topk_ids"][n], full["topk_ids"][row])
+        assert np.array_equal(res["window_ids"][n], full["window_ids"][row])
+        assert np.array_equal(res["out"][n], full["out"][row])
+        assert np.array_equal(res["lse"][n], full["lse"][row])
+
+
+@pytest.mark.parametrize("mode,pad", [(O.IN_SEQ, False), (O.ROUND_ROBIN, True)])
+def test_all_ranks_reranged_equal_the_single_rank_run_with_prefixes(mode, pad):
+    """The rank reconstruction holds for chunked prefill too (R-17)."""
+    wl1 = _tiny_wl(mode, 1, 0, pad, lens=(5, 7, 12), compress=4, window=3).with_(prefix=(8, 0, 10))
+    inp = S.stream_inputs(wl1)
+    m1 = O.cp_metadata(wl1.qsl, wl1.seq_lens, 1, 0, mode, pad)
+    full = O.run_path(m1, {**inp, **S.query_inputs(wl1, m1["token_map"])}, wl1)
+    cp = 3
+    parts = []
+    for r in range(cp):
+        wl = wl1.with_(cp=cp, rank=r)
+        m = O.cp_metadata(wl.qsl, wl.seq_lens, cp, r, mode, pad)
+        res = O.run_path(m, {**inp, **S.query_inputs(wl, m["token_map"])}, wl)
+        nrows = m["tokens_per_rank"] if pad else m["n_local_real"]
+        part = np.zeros((nrows, wl.H, wl.Dv))
+        part[:m["n_local_real"]] = res["out"]
+        parts.append(part)
+    back = O.rerange(np.concatenate(parts), wl1.T, cp, mode, pad)
+    assert np.allclose(back, full["out"], rtol=1e-12, atol=1e-15)

@@ -212,8 +212,83 @@ def test_in_seq_rerange_is_identity():
 
 def test_rejects_bad_arguments():
     with pytest.raises(ValueError):
-        O.cp_metadata([0, 4, 6], [4, 3], 2, 0, O.IN_SEQ, False)      # not pure prefill
+        O.cp_metadata([0, 4, 6], [4, 1], 2, 0, O.IN_SEQ, False)      # seq_lens below the query length
     with pytest.raises(ValueError):
         O.cp_metadata([0, 4, 6], [4, 2], 2, 2, O.IN_SEQ, False)      # rank out of range
     with pytest.raises(ValueError):
         O.cp_metadata([1, 4, 6], [3, 2], 2, 0, O.IN_SEQ, False)      # qsl[0] != 0
+
+
+# ----------------------------------------------------------------------------- chunked prefill
+# R-17: request b carries P_b = seq_lens[b] - n_b cached tokens; its KV segment is
+# seq_lens[b] rows long (prefix first), segments follow in request order, and query g of the
+# request sits at KV position P_b + g.  With P_b = 0 every rule above is unchanged.
+
+def _random_prefixed(seed, n):
+    g = np.random.default_rng(seed)
+    for lens in _random_batches(seed, n):
+        yield lens, [int(x) for x in g.integers(0, 30, size=len(lens))]
+
+
+def test_hand_worked_chunked_prefill():
+    """Queries [5,3,3] after cached prefixes [2,0,4] (seq_lens [7,3,7]), cp 3, tokens_per_rank 4.
+
+    KV segments start at rows 0, 7, 10 (17 rows in all).  Contiguous: rank 0 holds tokens 0..3,
+    the first four queries of request 0 at KV positions 2..5, so its last query sees 6 keys; a
+    later request contributes only its cached prefix (request 1 none, request 2 four rows);
+    rank 1 holds token 4 (position 6: 7 keys) and request 1; rank 2 holds request 2, whose last
+    query sees 4 + 3 keys, so the last rank sees every segment whole.
+    Round-robin: rank 0 {0,3,6,9}: last local queries of the requests sit at positions 5, 1, 5.
+    """
+    lens, prefix = [5, 3, 3], [2, 0, 4]
+    seq = [l + p for l, p in zip(lens, prefix)]
+    qsl = _qsl(lens)
+    want_in_seq = {
+        0: ([0, 4, 4, 4], [6, 0, 4], [0, 6, 6, 10], [3, 4, 5, 6]),
+        1: ([0, 1, 4, 4], [7, 3, 4], [0, 7, 10, 14], [7, 1, 2, 3]),
+        2: ([0, 0, 0, 3], [7, 3, 7], [0, 7, 10, 17], [5, 6, 7]),
+    }
+    for r, (lq, ls, lk, ext) in want_in_seq.items():
+        m = O.cp_metadata(qsl, seq, 3, r, O.IN_SEQ, False)
+        assert (list(m["local_query_start_loc"]), list(m["local_seq_lens"]),
+                list(m["local_kv_start_loc"])) == (lq, ls, lk)
+        assert [E for (_, E, _) in O.query_views(m)] == ext
+    want_rr = {
+        0: ([0, 2, 3, 4], [6, 2, 6], [3, 6, 2, 6]),
+        1: ([0, 2, 3, 4], [7, 3, 7], [4, 7, 3, 7]),
+        2: ([0, 1, 2, 3], [5, 1, 5], [5, 1, 5]),
+    }
+    for r, (lq, ls, ext) in want_rr.items():
+        m = O.cp_metadata(qsl, seq, 3, r, O.ROUND_ROBIN, False)
+        assert list(m["local_query_start_loc"]) == lq
+        assert list(m["local_seq_lens"]) == ls
+        assert list(m["local_kv_start_loc"]) == [0, 7, 10, 17]
+        assert [E for (_, E, _) in O.query_views(m)] == ext
+
+
+@pytest.mark.parametrize("mode,pad", MODES)
+def test_extents_with_prefixes_are_kv_positions_plus_one(mode, pad):
+    """Every local query sees its request's KV segment up to and including its own position."""
+    for lens, prefix in _random_prefixed(8, 30):
+        qsl = _qsl(lens)
+        seq = [l + p for l, p in zip(lens, prefix)]
+        kv_start = _qsl(seq)
+        for cp in (1, 2, 3, 5):
+            for r in range(cp):
+                m = O.cp_metadata(qsl, seq, cp, r, mode, pad)
+                toks = m["token_map"][m["token_map"] >= 0]
+                views = O.query_views(m)
+                assert len(views) == len(toks)
+                for t, (b, E, kv0) in zip(toks, views):
+                    assert qsl[b] <= t < qsl[b + 1]
+                    assert E == prefix[b] + (t - qsl[b]) + 1
+                    assert kv0 == kv_start[b]
+
+
+def test_last_rank_sees_every_segment_with_prefixes():
+    for lens, prefix in _random_prefixed(9, 30):
+        seq = [l + p for l, p in zip(lens, prefix)]
+        for cp in (1, 2, 4):
+            m = O.cp_metadata(_qsl(lens), seq, cp, cp - 1, O.IN_SEQ, False)
+            assert list(m["local_seq_lens"]) == seq
+            assert list(m["local_kv_start_loc"]) == list(_qsl(seq))
