@@ -169,7 +169,8 @@ typedef struct {
 /* Workspace bytes the call needs (0 if the arguments are invalid; see dsa_last_error). */
 size_t dsa_indexer_topk_workspace(const dsa_indexer_topk_args* args);
 
-/* Scores then top-k, both on `stream`. */
+/* Scores then top-k, both on `stream`. Rows with at most `topk` visible keys are taken whole
+ * by the top-k, so the indexer computes no scores for them (their workspace row is untouched). */
 dsa_status dsa_indexer_topk(const dsa_indexer_topk_args* args, void* stream);
 
 /* The two halves separately, on caller-provided score rows: scores [nq, ld] float32 with

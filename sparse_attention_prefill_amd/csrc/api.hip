@@ -24,7 +24,7 @@ dsa_status check_launch(const char* what) {
 dsa_status launch_cp_metadata(const int32_t*, const int32_t*, int, int, int, int, int, int32_t*, int32_t*, int32_t*,
                               int32_t*, int32_t*, int32_t*, hipStream_t);
 dsa_status launch_rerange(const void*, void*, int, int64_t, int, int, int, int, int, hipStream_t);
-dsa_status launch_indexer_scores(const dsa_indexer_topk_args*, float*, int64_t, int, hipStream_t);
+dsa_status launch_indexer_scores(const dsa_indexer_topk_args*, float*, int64_t, int, int, hipStream_t);
 dsa_status launch_topk(const dsa_indexer_topk_args*, const float*, int64_t, int, hipStream_t);
 dsa_status launch_sparse_attn(const dsa_sparse_attn_args*, hipStream_t);
 
@@ -127,7 +127,7 @@ dsa_status dsa_indexer_scores(const dsa_indexer_topk_args* a, float* scores, int
   if (a->nq == 0) return DSA_OK;
   if (!scores || !aligned16(scores)) return fail(DSA_ERR_INVALID_ARG, "indexer_scores: scores NULL or misaligned");
   if (ld < max_visible(a) || ld % 4 != 0) return fail(DSA_ERR_INVALID_ARG, "indexer_scores: ld too small or not % 4");
-  return launch_indexer_scores(a, scores, ld, max_visible(a), as_stream(stream));
+  return launch_indexer_scores(a, scores, ld, max_visible(a), 0, as_stream(stream));
 }
 
 dsa_status dsa_topk_from_scores(const dsa_indexer_topk_args* a, const float* scores, int64_t ld, void* stream) {
@@ -150,7 +150,8 @@ dsa_status dsa_indexer_topk(const dsa_indexer_topk_args* a, void* stream) {
     return fail(DSA_ERR_WORKSPACE, "indexer_topk: workspace missing, misaligned or smaller than "
                                        "dsa_indexer_topk_workspace()");
   float* scores = static_cast<float*>(a->workspace);
-  st = launch_indexer_scores(a, scores, score_ld(a), max_visible(a), as_stream(stream));
+  // rows with at most topk visible keys are taken whole by the top-k: the indexer skips them
+  st = launch_indexer_scores(a, scores, score_ld(a), max_visible(a), a->topk, as_stream(stream));
   if (st != DSA_OK) return st;
   return launch_topk(a, scores, score_ld(a), max_visible(a), as_stream(stream));
 }

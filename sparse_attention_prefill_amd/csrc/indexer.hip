@@ -39,7 +39,8 @@ template <typename T>
 __global__ __launch_bounds__(kGenThreads) void indexer_generic(
     const T* __restrict__ qi, const float* __restrict__ w, const T* __restrict__ ki, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ used_kv, const int32_t* __restrict__ cu_kv, int batch, int stride, int ratio,
-    int nq, int nk, int H, int D, int max_vis, float* __restrict__ scores, int64_t ld, int32_t* __restrict__ err_flag) {
+    int nq, int nk, int H, int D, int max_vis, int skip_le, float* __restrict__ scores, int64_t ld,
+    int32_t* __restrict__ err_flag) {
   extern __shared__ float sq[];  // [H*D] query block, then [H] weights
   const int i = blockIdx.y;
   QueryView v;
@@ -49,6 +50,7 @@ __global__ __launch_bounds__(kGenThreads) void indexer_generic(
     if (threadIdx.x == 0 && blockIdx.x == 0) raise_flag(err_flag, DSA_DEVERR_EXTENT);
     return;
   }
+  if (ev <= skip_le) return;  // the top-k keeps every visible key of this row without its scores
   for (int e = threadIdx.x; e < H * D; e += kGenThreads) sq[e] = ld_elt(qi, int64_t(i) * H * D + e);
   for (int e = threadIdx.x; e < H; e += kGenThreads) sq[H * D + e] = w[int64_t(i) * H + e];
   __syncthreads();
@@ -104,7 +106,8 @@ __global__ __launch_bounds__(kThreads, FP8 ? 4 : 1) void indexer_mfma(
     const unsigned char* __restrict__ qi, const float* __restrict__ q_scale, const float* __restrict__ w,
     const unsigned char* __restrict__ ki, const float* __restrict__ k_scale, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ used_kv, const int32_t* __restrict__ cu_kv, int batch, int stride, int ratio, int nq,
-    int nk, int max_vis, int chunk_keys, float* __restrict__ scores, int64_t ld, int32_t* __restrict__ err_flag) {
+    int nk, int max_vis, int chunk_keys, int skip_le, float* __restrict__ scores, int64_t ld,
+    int32_t* __restrict__ err_flag) {
   using C = IdxCfg<FP8>;
   __shared__ __attribute__((aligned(16))) unsigned char tiles[2 * C::kTileBytes];
   __shared__ __attribute__((aligned(16))) float ks_tile[2][FP8 ? kKeyTile : 4];
@@ -123,7 +126,8 @@ __global__ __launch_bounds__(kThreads, FP8 ? 4 : 1) void indexer_mfma(
     ev = ratio > 1 ? v.E / ratio : v.E;
     ok = v.E >= 1 && ev <= max_vis && v.kv0 >= 0 && int64_t(v.kv0) + ev <= nk;
     if (!ok && lane == 0) raise_flag(err_flag, DSA_DEVERR_EXTENT);
-    if (ok) {
+    // rows the top-k keeps whole (ev <= skip_le) need no scores: they join no key range
+    if (ok && ev > skip_le) {
       lo = v.kv0;
       hi = v.kv0 + ev;
     }
@@ -287,8 +291,8 @@ __global__ __launch_bounds__(kThreads, FP8 ? 4 : 1) void indexer_mfma(
 }  // namespace
 
 dsa_status launch_indexer_scores(const dsa_indexer_topk_args* a, float* scores, int64_t ld, int max_vis,
-                                 hipStream_t stream) {
-  if (a->nq == 0) return DSA_OK;
+                                 int skip_le, hipStream_t stream) {
+  if (a->nq == 0 || max_vis <= skip_le) return DSA_OK;
   const int stride = a->q_stride, ratio = a->compress_ratio;
   if (a->n_heads == kHi && a->head_dim == kDi && (a->dtype == DSA_BF16 || a->dtype == DSA_FP8_E4M3)) {
     // chunks of 2048 keys fill the GPU for short query batches; long batches take larger chunks
@@ -301,12 +305,12 @@ dsa_status launch_indexer_scores(const dsa_indexer_topk_args* a, float* scores, 
       hipLaunchKernelGGL(indexer_mfma<false>, grid, dim3(kThreads), 0, stream,
                          static_cast<const unsigned char*>(a->q_idx), a->q_scale, a->weights,
                          static_cast<const unsigned char*>(a->k_idx), a->k_scale, a->cu_seqlens_q, a->seqused_kv,
-                         a->cu_seqlens_kv, a->batch, stride, ratio, a->nq, a->nk, max_vis, chunk_keys, scores, ld, a->err_flag);
+                         a->cu_seqlens_kv, a->batch, stride, ratio, a->nq, a->nk, max_vis, chunk_keys, skip_le, scores, ld, a->err_flag);
     } else {
       hipLaunchKernelGGL(indexer_mfma<true>, grid, dim3(kThreads), 0, stream,
                          static_cast<const unsigned char*>(a->q_idx), a->q_scale, a->weights,
                          static_cast<const unsigned char*>(a->k_idx), a->k_scale, a->cu_seqlens_q, a->seqused_kv,
-                         a->cu_seqlens_kv, a->batch, stride, ratio, a->nq, a->nk, max_vis, chunk_keys, scores, ld, a->err_flag);
+                         a->cu_seqlens_kv, a->batch, stride, ratio, a->nq, a->nk, max_vis, chunk_keys, skip_le, scores, ld, a->err_flag);
     }
     return check_launch("indexer_mfma");
   }
@@ -319,12 +323,12 @@ dsa_status launch_indexer_scores(const dsa_indexer_topk_args* a, float* scores, 
     hipLaunchKernelGGL(indexer_generic<float>, grid, dim3(kGenThreads), lds, stream,
                        static_cast<const float*>(a->q_idx), a->weights, static_cast<const float*>(a->k_idx),
                        a->cu_seqlens_q, a->seqused_kv, a->cu_seqlens_kv, a->batch, stride, ratio, a->nq, a->nk,
-                       a->n_heads, a->head_dim, max_vis, scores, ld, a->err_flag);
+                       a->n_heads, a->head_dim, max_vis, skip_le, scores, ld, a->err_flag);
   } else if (a->dtype == DSA_BF16) {
     hipLaunchKernelGGL(indexer_generic<uint16_t>, grid, dim3(kGenThreads), lds, stream,
                        static_cast<const uint16_t*>(a->q_idx), a->weights, static_cast<const uint16_t*>(a->k_idx),
                        a->cu_seqlens_q, a->seqused_kv, a->cu_seqlens_kv, a->batch, stride, ratio, a->nq, a->nk,
-                       a->n_heads, a->head_dim, max_vis, scores, ld, a->err_flag);
+                       a->n_heads, a->head_dim, max_vis, skip_le, scores, ld, a->err_flag);
   } else {
     return fail(DSA_ERR_UNSUPPORTED, "indexer: unknown dtype");
   }

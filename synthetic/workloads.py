@@ -115,6 +115,11 @@ WORKLOADS = {
         "bf16", 2048, window=128, compress=4,
         notes="8 requests U[1024,16384], padded round-robin cp 4 rank 1; x4-compressed indexer, top-k 2048 "
               "plus a 128-token window"),
+    "rr_cp4_r1_var8_cmp128": Workload(
+        "rr_cp4_r1_var8_cmp128", 7, _var_lens(), 4, 1, "round_robin", True, 128, 576, 512, "bf16", 64, 128,
+        "bf16", 2048, window=128, compress=128,
+        notes="the same 8 requests and split with x128-compressed keys: at most 128 visible blocks per query, "
+              "so the top-k 2048 keeps every one, plus a 128-token window"),
 }
 
 

@@ -151,6 +151,8 @@ def _indexer_case(wl, variant, dev, rows_cap=None):
     ("chunk_inseq_cp8_last_8k_p56k", {"lens": (1500,), "prefix": (3333,), "cp": 2, "rank": 0}),
     ("rr_cp8_r3_batch4", {"lens": (700, 130, 5), "prefix": (2500, 1, 90)}),
     ("long_131k_fp8", {"lens": (1000, 9), "prefix": (5000, 4100), "cp": 2, "rank": 1}),
+    # x128-compressed keys: whole 128-token blocks become visible one at a time
+    ("rr_cp4_r1_var8_cmp128", {"lens": (5000, 300, 17000)}),
 ])
 def test_indexer_scores(name, kw, variant):
     dev = gpu()
