@@ -192,9 +192,11 @@ def main():
     stage = {name: float(np.mean([e[a].elapsed_time(e[b]) for e in evs]))
              for name, a, b in (("metadata", 0, 1), ("indexer_topk", 1, 2), ("sparse_attn", 2, 3), ("rerange", 3, 4))}
 
-    # stage split of indexer_topk through its two halves (same kernels, separate calls)
-    ld = ws_bytes // 4 // max(n_real, 1)
-    scores = ws.view(torch.float32)[:n_real * ld].view(n_real, ld)
+    # Stage split through the two-stage entry points (indexer score rows, then top-k over them) on a
+    # score matrix of their own. For rows longer than max(32768, K) the fused call above selects
+    # from candidate lists instead, so there indexer_topk is not the sum of these two.
+    vis_max = max_kv // wl.compress if wl.compress > 1 else max_kv
+    scores = torch.empty(max(n_real, 1), (vis_max + 63) // 64 * 64, dtype=torch.float32, device=dev)
     e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
     reps = max(3, args.steps // 2)
     split_ms = {"indexer": [], "topk": []}
@@ -261,6 +263,7 @@ def main():
                       "sparse_attn_frac": attn_flops / attn_s / 1e12 / attn_peak,
                       "indexer_frac": idx_flops / (indexer_ms * 1e-3) / 1e12 / idx_peak},
         "stages_ms": {**stage, "indexer": indexer_ms, "topk": topk_ms},
+        "indexer_topk_selection": "candidate lists" if vis_max > max(32768, wl.topk) else "score rows",
         "topk_hbm_frac": topk_bytes / (topk_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "work": {"indexer_pairs": pairs, "selected_rows": selected, "attn_gflop": attn_flops / 1e9,
                  "indexer_gflop": idx_flops / 1e9, "topk_mbytes": topk_bytes / 1e6},

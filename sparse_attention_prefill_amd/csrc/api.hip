@@ -1,6 +1,8 @@
 // Host entry points of libdsa: argument checks, sizes and kernel dispatch. See include/dsa.h.
 #include <string.h>
 
+#include <algorithm>
+
 #include <string>
 
 #include "dsa_internal.h"
@@ -24,8 +26,12 @@ dsa_status check_launch(const char* what) {
 dsa_status launch_cp_metadata(const int32_t*, const int32_t*, int, int, int, int, int, int32_t*, int32_t*, int32_t*,
                               int32_t*, int32_t*, int32_t*, hipStream_t);
 dsa_status launch_rerange(const void*, void*, int, int64_t, int, int, int, int, int, hipStream_t);
-dsa_status launch_indexer_scores(const dsa_indexer_topk_args*, float*, int64_t, int, int, hipStream_t);
+dsa_status launch_indexer_scores(const dsa_indexer_topk_args*, float*, int64_t, int, int, const CandidateMode*,
+                                 hipStream_t);
 dsa_status launch_topk(const dsa_indexer_topk_args*, const float*, int64_t, int, hipStream_t);
+dsa_status launch_topk_theta(const dsa_indexer_topk_args*, int, const CandidateMode&, hipStream_t);
+dsa_status launch_topk_candidates(const dsa_indexer_topk_args*, const float*, int64_t, int, const CandidateMode&,
+                                  float*, int64_t, int, hipStream_t);
 dsa_status launch_sparse_attn(const dsa_sparse_attn_args*, hipStream_t);
 
 namespace {
@@ -39,6 +45,33 @@ int max_visible(const dsa_indexer_topk_args* a) {
 int64_t score_ld(const dsa_indexer_topk_args* a) {
   const int64_t mv = max_visible(a) > 0 ? max_visible(a) : 1;
   return (mv + 63) / 64 * 64;
+}
+
+// Candidate mode (rows longer than max(kFuseMin, topk) are selected from lists of their best
+// scores, see topk.hip): only with the 64 x 128 matrix-core indexer.
+bool candidate_mode(const dsa_indexer_topk_args* a) {
+  const bool mfma = a->n_heads == 64 && a->head_dim == 128 && (a->dtype == DSA_BF16 || a->dtype == DSA_FP8_E4M3);
+  return mfma && max_visible(a) > std::max(kFuseMin, a->topk);
+}
+// Workspace of candidate mode: per row a 128 KB slot (a score row of kFuseMin floats, or a list
+// of kFuseCap entries), thresholds and list lengths, and the refill scratch rows.
+struct CandLayout {
+  size_t slots, theta, n_cand, scratch, total;
+  int n_scratch;
+  int64_t sld;
+};
+CandLayout cand_layout(const dsa_indexer_topk_args* a) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  CandLayout L;
+  const size_t nq = size_t(a->nq > 0 ? a->nq : 1);
+  L.slots = 0;
+  L.theta = up(nq * size_t(kFuseCap) * sizeof(uint2));
+  L.n_cand = L.theta + up(nq * sizeof(uint32_t));
+  L.scratch = L.n_cand + up(nq * sizeof(int32_t));
+  L.n_scratch = std::min(int(nq), kRefillBlocks);
+  L.sld = score_ld(a);
+  L.total = L.scratch + size_t(L.n_scratch) * size_t(L.sld) * sizeof(float);
+  return L;
 }
 
 dsa_status check_indexer_args(const dsa_indexer_topk_args* a, bool need_out) {
@@ -117,6 +150,7 @@ dsa_status dsa_build_cp_metadata(const int32_t* query_start_loc, const int32_t* 
 size_t dsa_indexer_topk_workspace(const dsa_indexer_topk_args* a) {
   clear_error();
   if (check_indexer_args(a, false) != DSA_OK) return 0;
+  if (candidate_mode(a)) return cand_layout(a).total;
   return size_t(a->nq > 0 ? a->nq : 1) * size_t(score_ld(a)) * sizeof(float);
 }
 
@@ -127,7 +161,7 @@ dsa_status dsa_indexer_scores(const dsa_indexer_topk_args* a, float* scores, int
   if (a->nq == 0) return DSA_OK;
   if (!scores || !aligned16(scores)) return fail(DSA_ERR_INVALID_ARG, "indexer_scores: scores NULL or misaligned");
   if (ld < max_visible(a) || ld % 4 != 0) return fail(DSA_ERR_INVALID_ARG, "indexer_scores: ld too small or not % 4");
-  return launch_indexer_scores(a, scores, ld, max_visible(a), 0, as_stream(stream));
+  return launch_indexer_scores(a, scores, ld, max_visible(a), 0, nullptr, as_stream(stream));
 }
 
 dsa_status dsa_topk_from_scores(const dsa_indexer_topk_args* a, const float* scores, int64_t ld, void* stream) {
@@ -145,15 +179,34 @@ dsa_status dsa_indexer_topk(const dsa_indexer_topk_args* a, void* stream) {
   dsa_status st = check_indexer_args(a, true);
   if (st != DSA_OK) return st;
   if (a->nq == 0) return DSA_OK;
-  const size_t need = size_t(a->nq) * size_t(score_ld(a)) * sizeof(float);
-  if (!a->workspace || a->workspace_bytes < need || !aligned16(a->workspace))
-    return fail(DSA_ERR_WORKSPACE, "indexer_topk: workspace missing, misaligned or smaller than "
+  const bool cmode = candidate_mode(a);
+  const size_t need = cmode ? cand_layout(a).total : size_t(a->nq) * size_t(score_ld(a)) * sizeof(float);
+  if (!a->workspace || a->workspace_bytes < need || (reinterpret_cast<uintptr_t>(a->workspace) & 255u))
+    return fail(DSA_ERR_WORKSPACE, "indexer_topk: workspace missing, not 256-byte aligned or smaller than "
                                        "dsa_indexer_topk_workspace()");
-  float* scores = static_cast<float*>(a->workspace);
-  // rows with at most topk visible keys are taken whole by the top-k: the indexer skips them
-  st = launch_indexer_scores(a, scores, score_ld(a), max_visible(a), a->topk, as_stream(stream));
+  hipStream_t s = as_stream(stream);
+  if (!cmode) {
+    float* scores = static_cast<float*>(a->workspace);
+    // rows with at most topk visible keys are taken whole by the top-k: the indexer skips them
+    st = launch_indexer_scores(a, scores, score_ld(a), max_visible(a), a->topk, nullptr, s);
+    if (st != DSA_OK) return st;
+    return launch_topk(a, scores, score_ld(a), max_visible(a), s);
+  }
+  const CandLayout L = cand_layout(a);
+  char* ws = static_cast<char*>(a->workspace);
+  CandidateMode cm;
+  cm.fuse_above = std::max(kFuseMin, a->topk);
+  cm.theta = reinterpret_cast<uint32_t*>(ws + L.theta);
+  cm.n_cand = reinterpret_cast<int32_t*>(ws + L.n_cand);
+  cm.cand = reinterpret_cast<uint2*>(ws + L.slots);
+  cm.cap = kFuseCap;
+  float* score_rows = reinterpret_cast<float*>(ws + L.slots);  // short rows: kFuseMin floats per slot
+  st = launch_topk_theta(a, max_visible(a), cm, s);
   if (st != DSA_OK) return st;
-  return launch_topk(a, scores, score_ld(a), max_visible(a), as_stream(stream));
+  st = launch_indexer_scores(a, score_rows, kFuseMin, max_visible(a), a->topk, &cm, s);
+  if (st != DSA_OK) return st;
+  return launch_topk_candidates(a, score_rows, kFuseMin, max_visible(a), cm, reinterpret_cast<float*>(ws + L.scratch),
+                                L.sld, L.n_scratch, s);
 }
 
 dsa_status dsa_sparse_attn(const dsa_sparse_attn_args* a, void* stream) {

@@ -97,6 +97,42 @@ __device__ inline bool query_view(const int32_t* __restrict__ cu_q, const int32_
   return true;
 }
 
+// ---------------------------------------------------------------------------------------------
+// Indexer + top-k without score rows for long rows. A row with more than fuse_above visible keys
+// (fuse_above = max(kFuseMin, K)) is a candidate row: a sample of its scores sets a threshold,
+// the indexer appends only the scores at or above it to the row's list, and the top-k selects
+// from the list. Shorter rows keep score rows of kFuseMin floats in the same per-row slot.
+// ---------------------------------------------------------------------------------------------
+constexpr int kFuseMin = 32768;   // longest score row (keys) outside candidate mode
+constexpr int kFuseCap = 16384;   // list entries per row: 8 bytes each, the size of that score row
+constexpr int kRefillBlocks = 256;  // workgroups (and scratch rows) recomputing unusable lists
+
+struct CandidateMode {
+  int fuse_above;     // rows with more visible keys are candidate rows
+  uint32_t* theta;    // [nq] thresholds as order keys
+  int32_t* n_cand;    // [nq] list lengths (entries past cap are dropped but counted)
+  uint2* cand;        // [nq, cap] (score bits, position)
+  int cap;
+};
+
+// Order-preserving 32-bit keys of float scores: -0.0 and +0.0 -> 0x80000000; a larger float
+// gives a larger key; finite floats stay above 2^23.
+__device__ inline uint32_t order_key_bits(uint32_t u) {
+  const uint32_t m = u & 0x7FFFFFFFu;
+  return (u >> 31) ? 0x80000000u - m : 0x80000000u + m;
+}
+__device__ inline uint32_t order_key(float f) { return order_key_bits(__float_as_uint(f)); }
+// the float whose key is k (k >= 2^23, i.e. not a NaN pattern)
+__device__ inline float key_to_float(uint32_t k) {
+  return k >= 0x80000000u ? __uint_as_float(k - 0x80000000u) : __uint_as_float((0x80000000u - k) | 0x80000000u);
+}
+
+__device__ inline uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
+// lanes below this one whose bit is set in m
+__device__ inline int lanes_below(uint64_t m) {
+  return int(__builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u)));
+}
+
 __device__ inline float bf16_bits_to_float(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
 // float -> bfloat16 bits, round to nearest even (finite inputs)

@@ -1,0 +1,123 @@
+// Lightning-indexer score arithmetic on gfx950 matrix cores, shared by every kernel that computes
+// a score, so that a (query, key) score is the same float whichever kernel produced it.
+//
+// [xLLM-CP] "feat: DeepSeek-V4 DSA context-parallel on NPU", Design, data-flow step (3):
+//   score(i, s) = sum_h w[i,h] * max(0, q_idx[i,h,:] . k_idx[s,:])   (64 heads x 128)
+// fp8 (E4M3): q_scale[i,h] is folded into the weight and k_scale[s] multiplies the head sum.
+//
+// Layout: one wave owns one query. A 32-key block takes two 32x32 MFMA chains (heads 0..31 and
+// 32..63) over the 128 dimensions; lane l holds key 32*nb + (l & 31) and, in each chain, heads
+// 8(r/4) + 4(l/32) + r%4 for r < 16. The head sum of both halves is combined across the halves,
+// so every lane ends with the full score of its key.
+#pragma once
+#include <type_traits>
+
+#include "dsa_internal.h"
+
+namespace dsa {
+
+constexpr int kIdxHeads = 64, kIdxDim = 128;
+
+// max(x, 0) on the float's bits: non-negative floats are non-negative ints, and negative floats
+// (-0.0 included) are negative ints, so an integer max with 0 is an exact ReLU in one VALU op
+// (a float max on MFMA results would first canonicalize its input).
+__device__ inline float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+template <bool FP8>
+struct IdxOps {
+  static constexpr int kKsteps = FP8 ? kIdxDim / 64 : kIdxDim / 16;  // 2 or 8 MFMAs per chain
+  static constexpr int kKeyBytes = FP8 ? kIdxDim : kIdxDim * 2;      // 128 or 256
+  using AOp = typename std::conditional<FP8, i32x8, bf16x8>::type;
+};
+
+// Query operands of row i for this lane: qa[m][ks] (heads 32m + (lane & 31)) and the weights of
+// the 16 heads the lane holds per chain, in output layout (times q_scale for fp8).
+template <bool FP8>
+__device__ inline void load_query_operands(const unsigned char* __restrict__ qi, const float* __restrict__ w,
+                                           const float* __restrict__ q_scale, int i,
+                                           typename IdxOps<FP8>::AOp (&qa)[2][IdxOps<FP8>::kKsteps],
+                                           float (&wv)[2][16]) {
+  const int lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const unsigned char* qrow = qi + (int64_t(i) * kIdxHeads + 32 * m + l32) * IdxOps<FP8>::kKeyBytes;
+#pragma unroll
+    for (int ks = 0; ks < IdxOps<FP8>::kKsteps; ++ks) {
+      if constexpr (FP8) {
+        const i32x4* p = reinterpret_cast<const i32x4*>(qrow + 64 * ks + 32 * half);
+        const i32x4 x0 = p[0], x1 = p[1];
+        qa[m][ks] = i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+      } else {
+        qa[m][ks] = *reinterpret_cast<const bf16x8*>(qrow + 2 * (16 * ks + 8 * half));
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int hh = 32 * m + 8 * (r >> 2) + 4 * half + (r & 3);
+      float wt = w[int64_t(i) * kIdxHeads + hh];
+      if constexpr (FP8) wt *= q_scale[int64_t(i) * kIdxHeads + hh];
+      wv[m][r] = wt;
+    }
+  }
+}
+
+// The two MFMA chains of one 32-key block; kb(ks) gives this lane's B operand of k-step ks
+// (bf16: dimensions 16ks + 8(lane/32) .. +8 of the lane's key; fp8: 64ks + 32(lane/32) .. +32).
+template <bool FP8, typename KB>
+__device__ inline void block_mfma_chains(const typename IdxOps<FP8>::AOp (&qa)[2][IdxOps<FP8>::kKsteps], KB&& kb,
+                                         f32x16& a0, f32x16& a1) {
+  a0 = f32x16{};
+  a1 = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < IdxOps<FP8>::kKsteps; ++ks) {
+    const typename IdxOps<FP8>::AOp b = kb(ks);
+    if constexpr (FP8) {
+      a0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[0][ks], b, a0, 0, 0, 0, 127, 0, 127);
+      a1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[1][ks], b, a1, 0, 0, 0, 127, 0, 127);
+    } else {
+      a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][ks], b, a0, 0, 0, 0);
+      a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][ks], b, a1, 0, 0, 0);
+    }
+  }
+}
+
+// sum over the 64 heads of w * relu(q . k) for the lane's key (both halves hold the result);
+// fp8 scores still need the key's scale
+__device__ inline float block_head_sum(const float (&wv)[2][16], const f32x16& a0, const f32x16& a1) {
+  float sacc = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    sacc = fmaf(wv[0][r], relu_bits(a0[r]), sacc);
+    sacc = fmaf(wv[1][r], relu_bits(a1[r]), sacc);
+  }
+  return sacc + __shfl_xor(sacc, 32, 64);
+}
+
+// B operand of k-step ks read straight from key row `row` in global memory
+template <bool FP8>
+__device__ inline typename IdxOps<FP8>::AOp key_operand_global(const unsigned char* __restrict__ ki, int row, int ks) {
+  const int half = (threadIdx.x & 63) >> 5;
+  const unsigned char* p = ki + int64_t(row) * IdxOps<FP8>::kKeyBytes;
+  if constexpr (FP8) {
+    const i32x4* q = reinterpret_cast<const i32x4*>(p + 64 * ks + 32 * half);
+    const i32x4 x0 = q[0], x1 = q[1];
+    return i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+  } else {
+    return *reinterpret_cast<const bf16x8*>(p + 2 * (16 * ks + 8 * half));
+  }
+}
+
+// Full score of key row `row` for the lane (every lane of the wave computes its own key; the
+// 32 lanes of each half must name the same 32 keys, lanes l and l + 32 the same key)
+template <bool FP8>
+__device__ inline float key_score_global(const typename IdxOps<FP8>::AOp (&qa)[2][IdxOps<FP8>::kKsteps],
+                                         const float (&wv)[2][16], const unsigned char* __restrict__ ki,
+                                         const float* __restrict__ k_scale, int row) {
+  f32x16 a0, a1;
+  block_mfma_chains<FP8>(qa, [&](int ks) { return key_operand_global<FP8>(ki, row, ks); }, a0, a1);
+  float s = block_head_sum(wv, a0, a1);
+  if constexpr (FP8) s *= k_scale[row];
+  return s + 0.f;  // -0.0 -> +0.0
+}
+
+}  // namespace dsa

@@ -18,10 +18,15 @@
 //    cross-half add. Tiles outside a wave's range are skipped by that wave.
 //    fp8: q_scale folds into the head weight and k_scale multiplies the head sum (both > 0);
 //    the tile's k_scale values are staged into LDS by the same direct loads as the keys.
+//    Candidate mode (rows longer than the fused-selection bound): instead of writing a score
+//    row, a wave keeps only the scores at or above its row's threshold theta (a 32-bit order
+//    key, see topk.hip) and appends them, with their positions, to the row's candidate list:
+//    hits are staged in a per-wave LDS buffer and flushed with one global atomic that claims
+//    the list slots. The top-k then selects from the list, so no full score row is ever written.
 //  * indexer_generic: float32 / bf16, small shapes (VALU, one thread per (query, key)).
 #include <algorithm>
 
-#include "dsa_internal.h"
+#include "index_score.h"
 
 namespace dsa {
 namespace {
@@ -69,8 +74,9 @@ __global__ __launch_bounds__(kGenThreads) void indexer_generic(
 // ---------------------------------------------------------------------------------------------
 // MFMA kernel: 64 heads x 128
 // ---------------------------------------------------------------------------------------------
-constexpr int kHi = 64, kDi = 128;
+constexpr int kHi = kIdxHeads, kDi = kIdxDim;
 constexpr int kWaves = 8, kThreads = kWaves * 64;
+constexpr int kStage = 256;  // candidate-mode LDS staging entries per wave
 constexpr int kKeyTile = 128;
 constexpr int kChunkKeys = 16 * kKeyTile;  // smallest key chunk per workgroup (grid.y splits longer ranges)
 constexpr int kTargetWorkgroups = 2048;    // chunks grow until the grid is about this large
@@ -82,11 +88,6 @@ struct IdxCfg {
   static constexpr int kTileBytes = kKeyTile * kKeyBytes;         // 8 or 16 KiB
   static constexpr int kLoads = kKeyTile * kChunks / kThreads;    // direct loads per lane per tile: 2 or 4
 };
-
-// max(x, 0) on the float's bits: non-negative floats are non-negative ints, and negative floats
-// (-0.0 included) are negative ints, so an integer max with 0 is an exact ReLU in one VALU op
-// (a float max on MFMA results would first canonicalize its input).
-__device__ inline float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
 // Physical 16-byte chunk of logical chunk c of key row n in an LDS tile. 256-byte rows (bf16):
 // XOR with n & 15, so the 16 rows read together by one MFMA operand load hit 16 distinct bank
@@ -101,17 +102,21 @@ __device__ inline int kswz(int n, int c) {
 // bf16: one workgroup per CU (its 64 x 128 query operand takes 64 VGPRs per lane), with the
 // epilogue software-pipelined against the next block's MFMAs. fp8: two workgroups per CU
 // (4 waves per SIMD, at most 128 VGPRs), which hides more than the pipelining does.
-template <bool FP8>
+// Candidate mode (CAND): rows with more than fuse_above visible keys append their scores at or
+// above theta[i] to cand[i * cand_cap ...] (count in n_cand[i]); shorter rows write score rows.
+template <bool FP8, bool CAND>
 __global__ __launch_bounds__(kThreads, FP8 ? 4 : 1) void indexer_mfma(
     const unsigned char* __restrict__ qi, const float* __restrict__ q_scale, const float* __restrict__ w,
     const unsigned char* __restrict__ ki, const float* __restrict__ k_scale, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ used_kv, const int32_t* __restrict__ cu_kv, int batch, int stride, int ratio, int nq,
     int nk, int max_vis, int chunk_keys, int skip_le, float* __restrict__ scores, int64_t ld,
-    int32_t* __restrict__ err_flag) {
+    int32_t* __restrict__ err_flag, int fuse_above, const uint32_t* __restrict__ theta, int32_t* __restrict__ n_cand,
+    uint2* __restrict__ cand, int cand_cap) {
   using C = IdxCfg<FP8>;
   __shared__ __attribute__((aligned(16))) unsigned char tiles[2 * C::kTileBytes];
   __shared__ __attribute__((aligned(16))) float ks_tile[2][FP8 ? kKeyTile : 4];
   __shared__ int s_lo[kWaves], s_hi[kWaves];
+  __shared__ uint2 stage[CAND ? kWaves : 1][CAND ? kStage : 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave (known to the compiler)
@@ -151,33 +156,23 @@ __global__ __launch_bounds__(kThreads, FP8 ? 4 : 1) void indexer_mfma(
   if (uhi <= ulo || int64_t(blockIdx.y) * chunk_keys >= int64_t(uhi) - ulo) return;  // uniform
 
   // ---- A operand: this wave's query block, heads 32m + l32, d-slices per k-step ----
-  constexpr int kKsteps = FP8 ? kDi / 64 : kDi / 16;  // 2 or 8
-  typedef typename std::conditional<FP8, i32x8, bf16x8>::type AOp;
-  AOp qa[2][kKsteps];
+  constexpr int kKsteps = IdxOps<FP8>::kKsteps;  // 2 or 8
+  typename IdxOps<FP8>::AOp qa[2][kKsteps];
   float wv[2][16];  // weights of the 16 heads this lane holds per head block, in output layout
-  if (ok) {
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const unsigned char* qrow = qi + (int64_t(i) * kHi + 32 * m + l32) * (FP8 ? kDi : kDi * 2);
-#pragma unroll
-      for (int ks = 0; ks < kKsteps; ++ks) {
-        if constexpr (FP8) {
-          const i32x4* p = reinterpret_cast<const i32x4*>(qrow + 64 * ks + 32 * half);
-          const i32x4 x0 = p[0], x1 = p[1];
-          qa[m][ks] = i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-        } else {
-          qa[m][ks] = *reinterpret_cast<const bf16x8*>(qrow + 2 * (16 * ks + 8 * half));
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int hh = 32 * m + 8 * (r >> 2) + 4 * half + (r & 3);
-        float wt = w[int64_t(i) * kHi + hh];
-        if constexpr (FP8) wt *= q_scale[int64_t(i) * kHi + hh];
-        wv[m][r] = wt;
-      }
-    }
-  }
+  if (ok) load_query_operands<FP8>(qi, w, q_scale, i, qa, wv);
+
+  // candidate mode: this wave's row keeps scores whose order key is >= theta_k
+  const bool cand_row = CAND && ok && hi - lo > fuse_above;  // wave-uniform
+  const uint32_t theta_k = cand_row ? theta[i] : 0u;
+  int st_n = 0;  // entries staged in stage[wave] (wave-uniform)
+  auto flush = [&]() {
+    int base = 0;
+    if (lane == 0) base = atomicAdd(&n_cand[i], st_n);
+    base = __builtin_amdgcn_readfirstlane(base);
+    for (int j = lane; j < st_n; j += 64)
+      if (base + j < cand_cap) cand[int64_t(i) * cand_cap + base + j] = stage[wave][j];
+    st_n = 0;
+  };
 
 #pragma unroll 1
   for (int64_t cs = int64_t(blockIdx.y) * chunk_keys; cs < int64_t(uhi) - ulo; cs += int64_t(gridDim.y) * chunk_keys) {
@@ -232,36 +227,34 @@ __global__ __launch_bounds__(kThreads, FP8 ? 4 : 1) void indexer_mfma(
         // epilogue, so the VALU epilogue runs under the matrix-core work
         auto block_mfma = [&](int nb, f32x16& a0, f32x16& a1) {
           const int n = 32 * nb + l32;
-          a0 = f32x16{};
-          a1 = f32x16{};
-#pragma unroll
-          for (int ks = 0; ks < kKsteps; ++ks) {
+          block_mfma_chains<FP8>(qa, [&](int ks) {
             if constexpr (FP8) {
               const int c0 = 4 * ks + 2 * half;  // two 16-byte chunks: d in [64ks + 32half, +32)
               const i32x4 x0 = *reinterpret_cast<const i32x4*>(tb + n * C::kKeyBytes + kswz<C::kChunks>(n, c0) * 16);
               const i32x4 x1 = *reinterpret_cast<const i32x4*>(tb + n * C::kKeyBytes + kswz<C::kChunks>(n, c0 + 1) * 16);
-              const i32x8 kb = i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-              a0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[0][ks], kb, a0, 0, 0, 0, 127, 0, 127);
-              a1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[1][ks], kb, a1, 0, 0, 0, 127, 0, 127);
+              return i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
             } else {
               const int c = 2 * ks + half;
-              const bf16x8 kb = *reinterpret_cast<const bf16x8*>(tb + n * C::kKeyBytes + kswz<C::kChunks>(n, c) * 16);
-              a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][ks], kb, a0, 0, 0, 0);
-              a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][ks], kb, a1, 0, 0, 0);
+              return *reinterpret_cast<const bf16x8*>(tb + n * C::kKeyBytes + kswz<C::kChunks>(n, c) * 16);
             }
-          }
+          }, a0, a1);
         };
         // lane holds key 32nb + l32 and heads 32m + 8(r/4) + 4half + r%4
         auto block_epilogue = [&](int nb, const f32x16& a0, const f32x16& a1) {
-          float sacc = 0.f;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            sacc = fmaf(wv[0][r], relu_bits(a0[r]), sacc);
-            sacc = fmaf(wv[1][r], relu_bits(a1[r]), sacc);
-          }
-          sacc += __shfl_xor(sacc, 32, 64);
+          float sacc = block_head_sum(wv, a0, a1);
           const int key = key0 + 32 * nb + l32;
-          if (half == 0 && key >= lo_c && key < hi_c) {
+          const bool in = half == 0 && key >= lo_c && key < hi_c;
+          if (CAND && cand_row) {
+            if constexpr (FP8) sacc *= ks_tile[buf][32 * nb + l32];
+            sacc += 0.f;  // -0.0 -> +0.0
+            const bool hit = in && order_key(sacc) >= theta_k;
+            const uint64_t m = ballot(hit);
+            if (m) {
+              if (hit) stage[wave][st_n + lanes_below(m)] = make_uint2(__float_as_uint(sacc), uint32_t(key - q_origin));
+              st_n += __popcll(m);
+              if (st_n > kStage - 32) flush();
+            }
+          } else if (in) {
             if constexpr (FP8) sacc *= ks_tile[buf][32 * nb + l32];
             scores[int64_t(i) * ld + (key - q_origin)] = sacc + 0.f;  // -0.0 -> +0.0
           }
@@ -286,12 +279,13 @@ __global__ __launch_bounds__(kThreads, FP8 ? 4 : 1) void indexer_mfma(
       DSA_TILE_BARRIER_LDS();
     }
   }
+  if (CAND && cand_row && st_n > 0) flush();
 }
 
 }  // namespace
 
 dsa_status launch_indexer_scores(const dsa_indexer_topk_args* a, float* scores, int64_t ld, int max_vis,
-                                 int skip_le, hipStream_t stream) {
+                                 int skip_le, const CandidateMode* cm, hipStream_t stream) {
   if (a->nq == 0 || max_vis <= skip_le) return DSA_OK;
   const int stride = a->q_stride, ratio = a->compress_ratio;
   if (a->n_heads == kHi && a->head_dim == kDi && (a->dtype == DSA_BF16 || a->dtype == DSA_FP8_E4M3)) {
@@ -301,19 +295,23 @@ dsa_status launch_indexer_scores(const dsa_indexer_topk_args* a, float* scores, 
     const int64_t merge = std::max<int64_t>(1, groups * base_chunks / kTargetWorkgroups);
     const int chunk_keys = int(std::min<int64_t>(merge, base_chunks) * kChunkKeys);
     const dim3 grid(unsigned(groups), unsigned((max_vis + chunk_keys - 1) / chunk_keys));
+    const CandidateMode none{INT32_MAX, nullptr, nullptr, nullptr, 0};
+    const CandidateMode& c = cm ? *cm : none;
+#define DSA_IDX_ARGS                                                                                           \
+  static_cast<const unsigned char*>(a->q_idx), a->q_scale, a->weights, static_cast<const unsigned char*>(a->k_idx), \
+      a->k_scale, a->cu_seqlens_q, a->seqused_kv, a->cu_seqlens_kv, a->batch, stride, ratio, a->nq, a->nk, max_vis,  \
+      chunk_keys, skip_le, scores, ld, a->err_flag, c.fuse_above, c.theta, c.n_cand, c.cand, c.cap
     if (a->dtype == DSA_BF16) {
-      hipLaunchKernelGGL(indexer_mfma<false>, grid, dim3(kThreads), 0, stream,
-                         static_cast<const unsigned char*>(a->q_idx), a->q_scale, a->weights,
-                         static_cast<const unsigned char*>(a->k_idx), a->k_scale, a->cu_seqlens_q, a->seqused_kv,
-                         a->cu_seqlens_kv, a->batch, stride, ratio, a->nq, a->nk, max_vis, chunk_keys, skip_le, scores, ld, a->err_flag);
+      if (cm) hipLaunchKernelGGL((indexer_mfma<false, true>), grid, dim3(kThreads), 0, stream, DSA_IDX_ARGS);
+      else hipLaunchKernelGGL((indexer_mfma<false, false>), grid, dim3(kThreads), 0, stream, DSA_IDX_ARGS);
     } else {
-      hipLaunchKernelGGL(indexer_mfma<true>, grid, dim3(kThreads), 0, stream,
-                         static_cast<const unsigned char*>(a->q_idx), a->q_scale, a->weights,
-                         static_cast<const unsigned char*>(a->k_idx), a->k_scale, a->cu_seqlens_q, a->seqused_kv,
-                         a->cu_seqlens_kv, a->batch, stride, ratio, a->nq, a->nk, max_vis, chunk_keys, skip_le, scores, ld, a->err_flag);
+      if (cm) hipLaunchKernelGGL((indexer_mfma<true, true>), grid, dim3(kThreads), 0, stream, DSA_IDX_ARGS);
+      else hipLaunchKernelGGL((indexer_mfma<true, false>), grid, dim3(kThreads), 0, stream, DSA_IDX_ARGS);
     }
+#undef DSA_IDX_ARGS
     return check_launch("indexer_mfma");
   }
+  if (cm) return fail(DSA_ERR_UNSUPPORTED, "indexer: candidate lists need the 64 x 128 matrix-core kernel");
   if (a->dtype == DSA_FP8_E4M3) return fail(DSA_ERR_UNSUPPORTED, "indexer: fp8 needs 64 heads x 128");
   if (a->n_heads * a->head_dim > 8192 || a->n_heads > 256)
     return fail(DSA_ERR_UNSUPPORTED, "indexer: shape not supported by the generic kernel");

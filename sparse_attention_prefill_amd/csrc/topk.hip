@@ -23,7 +23,7 @@
 // is selected exactly, and the ids are emitted from LDS bitmaps. When the list ends up with
 // fewer than K keys or overflows, the row falls back to an exact histogram over the whole row
 // (then keys above b* go straight to the bitmaps and only b*'s keys are listed).
-#include "dsa_internal.h"
+#include "index_score.h"
 
 namespace dsa {
 namespace {
@@ -36,21 +36,6 @@ constexpr int kStreamCand = 5120; // list of the streamed path (two workgroups p
 constexpr int kSampleBlock = 512; // sample keys per wave on the streamed path
 constexpr int kStreamVec = 4;     // float4 loads in flight per thread on the single pass
 
-// -0.0 and +0.0 -> 0x80000000; larger float -> larger key; finite floats stay above 2^23.
-__device__ inline uint32_t order_key_bits(uint32_t u) {
-  const uint32_t m = u & 0x7FFFFFFFu;
-  return (u >> 31) ? 0x80000000u - m : 0x80000000u + m;
-}
-__device__ inline uint32_t order_key(float f) { return order_key_bits(__float_as_uint(f)); }
-// the float whose key is k (k >= 2^23, i.e. not a NaN pattern)
-__device__ inline float key_to_float(uint32_t k) {
-  return k >= 0x80000000u ? __uint_as_float(k - 0x80000000u) : __uint_as_float((0x80000000u - k) | 0x80000000u);
-}
-
-__device__ inline uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
-__device__ inline int lanes_below(uint64_t m) {
-  return int(__builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u)));
-}
 // A wave-uniform value the compiler must treat as new: bounds of fully unrolled loops are
 // re-derived per pass, so their per-iteration conditions are not kept alive across passes.
 __device__ inline int opaque(int v) {
@@ -196,13 +181,14 @@ template <int NT>
 __device__ inline bool row_setup(const int32_t* __restrict__ cu_q, const int32_t* __restrict__ used_kv,
                                  const int32_t* __restrict__ cu_kv, const int32_t* __restrict__ win_kv, int batch,
                                  int stride, int ratio, int max_vis, int row_cap, int K, int window, int kv_row_base,
-                                 int32_t* orow, int32_t* err_flag, RowInfo* ri) {
+                                 int32_t* orow, int32_t* err_flag, RowInfo* ri, int skip_above = INT32_MAX) {
   const int i = blockIdx.x, tid = threadIdx.x;
   const int k_tot = K + window;
   QueryView v;
   const bool have = query_view(cu_q, used_kv, cu_kv, batch, stride, i, &v);
   const int ev = have ? (ratio > 1 ? v.E / ratio : v.E) : 0;
-  if (!(have && v.E >= 1 && ev <= max_vis && ev <= row_cap)) {
+  if (have && v.E >= 1 && ev > skip_above && ev <= max_vis) return false;  // selected from a candidate list
+  if (!(have && v.E >= 1 && ev <= max_vis)) {
     if (tid == 0) raise_flag(err_flag, DSA_DEVERR_EXTENT);
     for (int j = tid; j < k_tot; j += NT) orow[j] = -1;
     return false;
@@ -217,6 +203,11 @@ __device__ inline bool row_setup(const int32_t* __restrict__ cu_q, const int32_t
   ri->base = kv_row_base + v.kv0;
   if (ev <= K) {  // every visible key
     for (int j = tid; j < K; j += NT) orow[j] = j < ev ? ri->base + j : -1;
+    return false;
+  }
+  if (ev > row_cap) {  // no kernel of this launch holds such a row
+    if (tid == 0) raise_flag(err_flag, DSA_DEVERR_EXTENT);
+    for (int j = tid; j < K; j += NT) orow[j] = -1;
     return false;
   }
   return true;
@@ -249,7 +240,8 @@ template <int NT, int EPT>
 __global__ __launch_bounds__(NT, NT == 1024 ? 8 : 1) void topk_reg_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ used_kv,
     const int32_t* __restrict__ cu_kv, const int32_t* __restrict__ win_kv, int batch, int stride, int ratio,
-    int max_vis, int K, int window, int kv_row_base, int32_t* __restrict__ out, int32_t* __restrict__ err_flag) {
+    int max_vis, int K, int window, int kv_row_base, int32_t* __restrict__ out, int32_t* __restrict__ err_flag,
+    int skip_above) {
   static_assert(EPT % 4 == 0 && EPT <= 64, "chunks come in groups of 4; one chunk per lane / thread");
   using Sh = RegShared<NT, EPT>;
   __shared__ Sh sh;
@@ -260,7 +252,7 @@ __global__ __launch_bounds__(NT, NT == 1024 ? 8 : 1) void topk_reg_kernel(
   int32_t* orow = out + int64_t(blockIdx.x) * (K + window);
   RowInfo ri;
   if (!row_setup<NT>(cu_q, used_kv, cu_kv, win_kv, batch, stride, ratio, max_vis, NT * EPT, K, window, kv_row_base,
-                     orow, err_flag, &ri))
+                     orow, err_flag, &ri, skip_above))
     return;
   const int ev = ri.ev;
   const float* srow = scores + int64_t(blockIdx.x) * ld;
@@ -440,21 +432,52 @@ struct StreamShared {
   int n_cand;
 };
 
-__global__ __launch_bounds__(kStreamNT, 8) void topk_stream_kernel(
-    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ used_kv,
-    const int32_t* __restrict__ cu_kv, const int32_t* __restrict__ win_kv, int batch, int stride, int ratio,
-    int max_vis, int K, int window, int kv_row_base, int32_t* __restrict__ out, int32_t* __restrict__ err_flag) {
+// Ascending ids base + position of the selected keys, from the bitmaps of the keys above tau
+// and equal to tau (the first `need` of those in position order): each thread owns a run of
+// 64-position chunks, and a block scan gives each run its output offset.
+template <int NT>
+__device__ __attribute__((always_inline)) inline void emit_from_bitmaps(const uint64_t* gt, const uint64_t* eq, int n_chunks, int need, int K,
+                                         int base, int32_t* __restrict__ orow, int* scan) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x;
+  const int per = (n_chunks + NT - 1) / NT;
+  const int c_begin = min(tid * per, n_chunks), c_end = min(c_begin + per, n_chunks);
+  int my_gt = 0, my_eq = 0;
+  for (int c = c_begin; c < c_end; ++c) {
+    my_gt += __popcll(gt[c]);
+    my_eq += __popcll(eq[c]);
+  }
+  int gt_before, eq_before, gt_tot, eq_tot;
+  block_excl_scan2<NW>(my_gt, my_eq, scan, &gt_before, &eq_before, &gt_tot, &eq_tot);
+  int pos = gt_before + min(eq_before, need);
+  int eq_rank = eq_before;
+  for (int c = c_begin; c < c_end; ++c) {
+    uint64_t e = eq[c], keep = 0;
+    while (e) {  // ties in position order, while the quota lasts
+      const uint64_t bit = e & (~e + 1ull);
+      if (eq_rank < need) keep |= bit;
+      ++eq_rank;
+      e ^= bit;
+    }
+    uint64_t s = gt[c] | keep;
+    while (s) {
+      const int b = __builtin_ctzll(s);
+      if (pos < K) orow[pos] = base + (c << 6) + b;
+      ++pos;
+      s &= s - 1;
+    }
+  }
+  const int n_sel = gt_tot + min(eq_tot, need);
+  for (int j = n_sel + tid; j < K; j += NT) orow[j] = -1;  // only if ties were short (cannot happen)
+}
+
+// Top-K of one score row srow[0, ev) (ev > K), streamed from memory by kStreamNT threads; row
+// storage is ld floats (loads stay below it). Writes orow[0, K) = base + position, ascending.
+__device__ __attribute__((always_inline)) inline void stream_select(const float* __restrict__ srow, int64_t ld, int ev, int K, int base,
+                                     int32_t* __restrict__ orow, StreamShared& sh) {
   constexpr int NT = kStreamNT, NW = NT / 64;
-  __shared__ StreamShared sh;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  int32_t* orow = out + int64_t(blockIdx.x) * (K + window);
-  RowInfo ri;
-  if (!row_setup<NT>(cu_q, used_kv, cu_kv, win_kv, batch, stride, ratio, max_vis, kMaxRow, K, window, kv_row_base,
-                     orow, err_flag, &ri))
-    return;
-  const int ev = ri.ev;
-  const float* srow = scores + int64_t(blockIdx.x) * ld;
   const int n_chunks = (ev + 63) >> 6;
   uint64_t* gt = sh.u.bits[0];
   uint64_t* eq = sh.u.bits[1];
@@ -686,37 +709,223 @@ __global__ __launch_bounds__(kStreamNT, 8) void topk_stream_kernel(
   }
   __syncthreads();
   const int need = sh.remaining;  // keys equal to tau to take (>= 1)
+  emit_from_bitmaps<NT>(gt, eq, n_chunks, need, K, base, orow, sh.scan);
+}
 
-  // ---- ascending ids from the bitmaps: each thread owns a run of chunks ----
-  const int per = (n_chunks + NT - 1) / NT;
-  const int c_begin = min(tid * per, n_chunks), c_end = min(c_begin + per, n_chunks);
-  int my_gt = 0, my_eq = 0;
-  for (int c = c_begin; c < c_end; ++c) {
-    my_gt += __popcll(gt[c]);
-    my_eq += __popcll(eq[c]);
-  }
-  int gt_before, eq_before, gt_tot, eq_tot;
-  block_excl_scan2<NW>(my_gt, my_eq, sh.scan, &gt_before, &eq_before, &gt_tot, &eq_tot);
-  int pos = gt_before + min(eq_before, need);
-  int eq_rank = eq_before;
-  for (int c = c_begin; c < c_end; ++c) {
-    uint64_t e = eq[c], keep = 0;
-    while (e) {  // ties in position order, while the quota lasts
-      const uint64_t bit = e & (~e + 1ull);
-      if (eq_rank < need) keep |= bit;
-      ++eq_rank;
-      e ^= bit;
+__global__ __launch_bounds__(kStreamNT, 8) void topk_stream_kernel(
+    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ used_kv,
+    const int32_t* __restrict__ cu_kv, const int32_t* __restrict__ win_kv, int batch, int stride, int ratio,
+    int max_vis, int K, int window, int kv_row_base, int32_t* __restrict__ out, int32_t* __restrict__ err_flag,
+    int skip_above) {
+  __shared__ StreamShared sh;
+  int32_t* orow = out + int64_t(blockIdx.x) * (K + window);
+  RowInfo ri;
+  if (!row_setup<kStreamNT>(cu_q, used_kv, cu_kv, win_kv, batch, stride, ratio, max_vis, kMaxRow, K, window,
+                            kv_row_base, orow, err_flag, &ri, skip_above))
+    return;
+  stream_select(scores + int64_t(blockIdx.x) * ld, ld, ri.ev, K, ri.base, orow, sh);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Rows selected from candidate lists (no score row in memory)
+// ---------------------------------------------------------------------------------------------
+constexpr int kThetaBins = 2048;                       // 11-bit digits of the sample select
+constexpr int kSampleTiles = 16;                       // sampled 128-key tiles per row
+constexpr int kSampleKeys = kSampleTiles * 128;        // 2048 sample scores per row
+constexpr int kCandNT = 1024;
+constexpr int kCandEPT = kFuseCap / kCandNT;           // 16 list entries per thread
+
+// Threshold of each candidate row (one wave per row, 8 rows per workgroup): the scores of 16
+// tiles of 128 consecutive keys spread evenly over the row, and theta = the 22-bit key prefix of
+// the sample's r-th largest score, r = ceil(3 K * 2048 / ev): about 3K of the row's keys reach
+// theta, K of them needed, the list holding kFuseCap. Also zeroes every row's list count.
+template <bool FP8>
+__global__ __launch_bounds__(512) void topk_theta_kernel(
+    const unsigned char* __restrict__ qi, const float* __restrict__ q_scale, const float* __restrict__ w,
+    const unsigned char* __restrict__ ki, const float* __restrict__ k_scale, const int32_t* __restrict__ cu_q,
+    const int32_t* __restrict__ used_kv, const int32_t* __restrict__ cu_kv, int batch, int stride, int ratio, int nq,
+    int nk, int max_vis, int K, int fuse_above, uint32_t* __restrict__ theta, int32_t* __restrict__ n_cand) {
+  __shared__ alignas(16) uint32_t hist[8][kThetaBins];
+  const int lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int i = blockIdx.x * 8 + wave;
+  if (i >= nq) return;  // no workgroup barrier below
+  if (lane == 0) n_cand[i] = 0;
+  QueryView v;
+  if (!query_view(cu_q, used_kv, cu_kv, batch, stride, i, &v)) return;
+  const int ev = ratio > 1 ? v.E / ratio : v.E;
+  if (v.E < 1 || ev <= fuse_above || ev > max_vis || v.kv0 < 0 || int64_t(v.kv0) + ev > nk) return;
+
+  typename IdxOps<FP8>::AOp qa[2][IdxOps<FP8>::kKsteps];
+  float wv[2][16];
+  load_query_operands<FP8>(qi, w, q_scale, i, qa, wv);
+  // block b = 4 * tile + sub covers positions start(tile) + 32 sub + [0, 32); lanes of half h keep
+  // the keys of block 2p + h
+  uint32_t sk[kSampleKeys / 64];
+#pragma unroll 1
+  for (int p = 0; p < kSampleKeys / 64; ++p) {
+    float sc[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int b = 2 * p + h, tile = b >> 2;
+      const int start = int(int64_t(tile) * (ev - 128) / (kSampleTiles - 1));
+      sc[h] = key_score_global<FP8>(qa, wv, ki, k_scale, v.kv0 + start + 32 * (b & 3) + l32);
     }
-    uint64_t s = gt[c] | keep;
-    while (s) {
-      const int b = __builtin_ctzll(s);
-      if (pos < K) orow[pos] = ri.base + (c << 6) + b;
-      ++pos;
-      s &= s - 1;
+    sk[p] = order_key(half ? sc[1] : sc[0]);
+  }
+  const int r_s = int(min<int64_t>(kSampleKeys, (int64_t(3) * K * kSampleKeys + ev - 1) / ev));
+  uint32_t* h = hist[wave];
+  int bin1, bin2, rem, cnt;
+  for (int b = 4 * lane; b < kThetaBins; b += 256) *reinterpret_cast<uint4*>(h + b) = uint4{0, 0, 0, 0};
+  lds_wait();
+#pragma unroll
+  for (int p = 0; p < kSampleKeys / 64; ++p) atomicAdd(&h[sk[p] >> 21], 1u);
+  lds_wait();
+  wave_select<kThetaBins>(h, r_s, &bin1, &rem, &cnt);
+  lds_wait();
+  for (int b = 4 * lane; b < kThetaBins; b += 256) *reinterpret_cast<uint4*>(h + b) = uint4{0, 0, 0, 0};
+  lds_wait();
+#pragma unroll
+  for (int p = 0; p < kSampleKeys / 64; ++p)
+    if (int(sk[p] >> 21) == bin1) atomicAdd(&h[(sk[p] >> 10) & (kThetaBins - 1)], 1u);
+  lds_wait();
+  wave_select<kThetaBins>(h, rem, &bin2, &rem, &cnt);
+  if (lane == 0) theta[i] = (uint32_t(bin1) << 21) | (uint32_t(bin2) << 10);
+}
+
+struct CandShared {
+  union {
+    alignas(16) uint32_t hist[kBins0];
+    uint64_t bits[2][kMaxRow / 64];  // keys above tau / equal to tau, one bit per position
+  } u;
+  alignas(16) uint32_t hist_r[kBinsR];
+  int scan[2 * (kCandNT / 64 + 1)];
+  uint32_t prefix;
+  int remaining;
+};
+
+// Exact top-K of a candidate row from its list (every key >= theta, with its position): the
+// three-digit radix select over the list in registers, then ids from position bitmaps. A row
+// whose list holds fewer than K entries or overflowed is left to topk_refill_kernel.
+__global__ __launch_bounds__(kCandNT, 2) void topk_cand_kernel(
+    const uint2* __restrict__ cand, const int32_t* __restrict__ n_cand, int cap, int fuse_above,
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ used_kv, const int32_t* __restrict__ cu_kv,
+    const int32_t* __restrict__ win_kv, int batch, int stride, int ratio, int max_vis, int K, int window,
+    int kv_row_base, int32_t* __restrict__ out, int32_t* __restrict__ err_flag) {
+  constexpr int NT = kCandNT;
+  __shared__ CandShared sh;
+  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  QueryView v;
+  const bool have = query_view(cu_q, used_kv, cu_kv, batch, stride, row, &v);
+  const int ev = have ? (ratio > 1 ? v.E / ratio : v.E) : 0;
+  if (!have || v.E < 1 || ev <= fuse_above || ev > max_vis) return;  // not a candidate row
+  int32_t* orow = out + int64_t(row) * (K + window);
+  RowInfo ri;
+  if (!row_setup<NT>(cu_q, used_kv, cu_kv, win_kv, batch, stride, ratio, max_vis, kMaxRow, K, window, kv_row_base,
+                     orow, err_flag, &ri))
+    return;
+  const int n = n_cand[row];
+  if (n < K || n > cap) return;
+
+  const uint2* crow = cand + int64_t(row) * cap;
+  uint32_t keys[kCandEPT];
+  int pos[kCandEPT];
+#pragma unroll
+  for (int j = 0; j < kCandEPT; ++j) {
+    const int c = j * NT + tid;
+    const uint2 e = c < n ? crow[c] : uint2{0u, 0u};
+    keys[j] = order_key_bits(e.x);
+    pos[j] = c < n ? int(e.y) : -1;
+  }
+  // digit 1
+  zero_words<NT>(sh.u.hist, kBins0);
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kCandEPT; ++j)
+    if (pos[j] >= 0) atomicAdd(&sh.u.hist[keys[j] >> 20], 1u);
+  __syncthreads();
+  if (wave == 0) {
+    int bin, rem, cnt;
+    wave_select<kBins0>(sh.u.hist, K, &bin, &rem, &cnt);
+    if (lane == 0) {
+      sh.prefix = uint32_t(bin) << 20;
+      sh.remaining = rem;
     }
   }
-  const int n_sel = gt_tot + min(eq_tot, need);
-  for (int j = n_sel + tid; j < K; j += NT) orow[j] = -1;  // only if ties were short (cannot happen)
+  // digits 2 and 3 over the registers
+#pragma unroll 1
+  for (int r = 0; r < 2; ++r) {
+    const int shift = 10 - 10 * r;
+    zero_words<NT>(sh.hist_r, kBinsR);
+    __syncthreads();
+    const uint32_t pfx = sh.prefix >> (shift + 10);
+#pragma unroll
+    for (int j = 0; j < kCandEPT; ++j)
+      if (pos[j] >= 0 && (keys[j] >> (shift + 10)) == pfx) atomicAdd(&sh.hist_r[(keys[j] >> shift) & (kBinsR - 1)], 1u);
+    __syncthreads();
+    if (wave == 0) {
+      int bin, rem, cnt;
+      wave_select<kBinsR>(sh.hist_r, sh.remaining, &bin, &rem, &cnt);
+      if (lane == 0) {
+        sh.prefix |= uint32_t(bin) << shift;
+        sh.remaining = rem;
+      }
+    }
+    __syncthreads();
+  }
+  const uint32_t tau = sh.prefix;
+  const int need = sh.remaining;
+  const int n_chunks = (ev + 63) >> 6;
+  uint64_t* gt = sh.u.bits[0];
+  uint64_t* eq = sh.u.bits[1];
+  for (int c = tid; c < n_chunks; c += NT) gt[c] = eq[c] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kCandEPT; ++j) {
+    if (pos[j] < 0) continue;
+    if (keys[j] > tau) atomicOr(&gt[pos[j] >> 6], 1ull << (pos[j] & 63));
+    else if (keys[j] == tau) atomicOr(&eq[pos[j] >> 6], 1ull << (pos[j] & 63));
+  }
+  __syncthreads();
+  emit_from_bitmaps<NT>(gt, eq, n_chunks, need, K, ri.base, orow, sh.scan);
+}
+
+// Candidate rows whose list fell short of K or overflowed: a persistent workgroup recomputes
+// each such row's scores (the same arithmetic as the indexer) into its own scratch row and
+// selects from it like topk_stream_kernel. Rows whose list was usable are skipped.
+template <bool FP8>
+__global__ __launch_bounds__(kStreamNT, 1) void topk_refill_kernel(
+    const unsigned char* __restrict__ qi, const float* __restrict__ q_scale, const float* __restrict__ w,
+    const unsigned char* __restrict__ ki, const float* __restrict__ k_scale, const int32_t* __restrict__ cu_q,
+    const int32_t* __restrict__ used_kv, const int32_t* __restrict__ cu_kv, int batch, int stride, int ratio, int nq,
+    int nk, int max_vis, int K, int window, int kv_row_base, int fuse_above, const int32_t* __restrict__ n_cand,
+    int cap, float* __restrict__ scratch, int64_t sld, int32_t* __restrict__ out) {
+  __shared__ StreamShared sh;
+  const int lane = threadIdx.x & 63, l32 = lane & 31, half = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  float* srow = scratch + int64_t(blockIdx.x) * sld;
+#pragma unroll 1
+  for (int row = blockIdx.x; row < nq; row += gridDim.x) {
+    QueryView v;
+    if (!query_view(cu_q, used_kv, cu_kv, batch, stride, row, &v)) continue;
+    const int ev = ratio > 1 ? v.E / ratio : v.E;
+    if (v.E < 1 || ev <= fuse_above || ev > max_vis || v.kv0 < 0 || int64_t(v.kv0) + ev > nk) continue;
+    const int n = n_cand[row];
+    if (n >= K && n <= cap) continue;
+    typename IdxOps<FP8>::AOp qa[2][IdxOps<FP8>::kKsteps];
+    float wv[2][16];
+    load_query_operands<FP8>(qi, w, q_scale, row, qa, wv);
+#pragma unroll 1
+    for (int b = wave; 32 * b < ev; b += kStreamNT / 64) {
+      const int p = 32 * b + l32;
+      const float sc = key_score_global<FP8>(qa, wv, ki, k_scale, v.kv0 + min(p, ev - 1));
+      if (half == 0 && p < ev) srow[p] = sc;
+    }
+    __syncthreads();  // the row's scores are visible to the workgroup
+    stream_select(srow, sld, ev, K, kv_row_base + v.kv0, out + int64_t(row) * (K + window), sh);
+    __syncthreads();  // before the next row overwrites the scratch row and the shared state
+  }
 }
 
 }  // namespace
@@ -728,7 +937,7 @@ dsa_status launch_topk(const dsa_indexer_topk_args* a, const float* scores, int6
   const dim3 grid(a->nq);
 #define DSA_TOPK_ARGS                                                                                          \
   scores, ld, a->cu_seqlens_q, a->seqused_kv, a->cu_seqlens_kv, a->window_kv_start, a->batch, a->q_stride,     \
-      a->compress_ratio, max_vis, a->topk, a->window, a->kv_row_base, a->topk_idx, a->err_flag
+      a->compress_ratio, max_vis, a->topk, a->window, a->kv_row_base, a->topk_idx, a->err_flag, INT32_MAX
 #define DSA_TOPK_REG(NT, E) hipLaunchKernelGGL((topk_reg_kernel<NT, E>), grid, dim3(NT), 0, stream, DSA_TOPK_ARGS)
   if (max_vis <= 256 * 16) DSA_TOPK_REG(256, 16);
   else if (max_vis <= 512 * 16) DSA_TOPK_REG(512, 16);
@@ -738,6 +947,49 @@ dsa_status launch_topk(const dsa_indexer_topk_args* a, const float* scores, int6
 #undef DSA_TOPK_REG
 #undef DSA_TOPK_ARGS
   return check_launch("topk_kernel");
+}
+
+// Candidate-list selection: thresholds (before the indexer), then, after it, the score rows of
+// short rows, the lists of candidate rows and the refill of rows whose list was unusable.
+dsa_status launch_topk_theta(const dsa_indexer_topk_args* a, int max_vis, const CandidateMode& cm,
+                             hipStream_t stream) {
+  if (a->nq == 0) return DSA_OK;
+  const dim3 grid((a->nq + 7) / 8);
+#define DSA_THETA_ARGS                                                                                        \
+  static_cast<const unsigned char*>(a->q_idx), a->q_scale, a->weights, static_cast<const unsigned char*>(a->k_idx), \
+      a->k_scale, a->cu_seqlens_q, a->seqused_kv, a->cu_seqlens_kv, a->batch, a->q_stride, a->compress_ratio, a->nq, \
+      a->nk, max_vis, a->topk, cm.fuse_above, cm.theta, cm.n_cand
+  if (a->dtype == DSA_FP8_E4M3) hipLaunchKernelGGL(topk_theta_kernel<true>, grid, dim3(512), 0, stream, DSA_THETA_ARGS);
+  else hipLaunchKernelGGL(topk_theta_kernel<false>, grid, dim3(512), 0, stream, DSA_THETA_ARGS);
+#undef DSA_THETA_ARGS
+  return check_launch("topk_theta_kernel");
+}
+
+dsa_status launch_topk_candidates(const dsa_indexer_topk_args* a, const float* score_rows, int64_t ld, int max_vis,
+                                  const CandidateMode& cm, float* scratch, int64_t sld, int n_scratch,
+                                  hipStream_t stream) {
+  if (a->nq == 0) return DSA_OK;
+  if (max_vis > kMaxRow) return fail(DSA_ERR_UNSUPPORTED, "topk: rows longer than 131072 keys");
+  const dim3 grid(a->nq);
+  hipLaunchKernelGGL((topk_reg_kernel<1024, 32>), grid, dim3(1024), 0, stream, score_rows, ld, a->cu_seqlens_q,
+                     a->seqused_kv, a->cu_seqlens_kv, a->window_kv_start, a->batch, a->q_stride, a->compress_ratio,
+                     max_vis, a->topk, a->window, a->kv_row_base, a->topk_idx, a->err_flag, cm.fuse_above);
+  dsa_status st = check_launch("topk_reg_kernel");
+  if (st != DSA_OK) return st;
+  hipLaunchKernelGGL(topk_cand_kernel, grid, dim3(kCandNT), 0, stream, cm.cand, cm.n_cand, cm.cap, cm.fuse_above,
+                     a->cu_seqlens_q, a->seqused_kv, a->cu_seqlens_kv, a->window_kv_start, a->batch, a->q_stride,
+                     a->compress_ratio, max_vis, a->topk, a->window, a->kv_row_base, a->topk_idx, a->err_flag);
+  st = check_launch("topk_cand_kernel");
+  if (st != DSA_OK) return st;
+#define DSA_REFILL_ARGS                                                                                       \
+  static_cast<const unsigned char*>(a->q_idx), a->q_scale, a->weights, static_cast<const unsigned char*>(a->k_idx), \
+      a->k_scale, a->cu_seqlens_q, a->seqused_kv, a->cu_seqlens_kv, a->batch, a->q_stride, a->compress_ratio, a->nq, \
+      a->nk, max_vis, a->topk, a->window, a->kv_row_base, cm.fuse_above, cm.n_cand, cm.cap, scratch, sld, a->topk_idx
+  const dim3 rgrid(n_scratch);
+  if (a->dtype == DSA_FP8_E4M3) hipLaunchKernelGGL(topk_refill_kernel<true>, rgrid, dim3(kStreamNT), 0, stream, DSA_REFILL_ARGS);
+  else hipLaunchKernelGGL(topk_refill_kernel<false>, rgrid, dim3(kStreamNT), 0, stream, DSA_REFILL_ARGS);
+#undef DSA_REFILL_ARGS
+  return check_launch("topk_refill_kernel");
 }
 
 }  // namespace dsa

@@ -235,12 +235,13 @@ def stream_inputs(wl: Workload, variant="normal"):
     return out
 
 
-def query_inputs(wl: Workload, tokens, variant="normal"):
+def query_inputs(wl: Workload, tokens, variant="normal", indexer_only=False):
     """Per-query tensors for the given global token ids (pads: id < 0 give zero rows).
 
     Returns q [n,H,D_qk], q_idx [n,H_i,D_i], w [n,H_i] float32, and q_scale [n,H_i] for fp8,
     filled token by token straight into the storage dtype.  Token t of request b is seeded by
-    its KV row kvsl[b] + prefix[b] + (t - qsl[b]) (= t without prefixes).
+    its KV row kvsl[b] + prefix[b] + (t - qsl[b]) (= t without prefixes).  indexer_only: q is
+    left out (the indexer tensors are the same values either way).
     """
     tokens = np.asarray(tokens, dtype=np.int64)
     n = len(tokens)
@@ -251,7 +252,7 @@ def query_inputs(wl: Workload, tokens, variant="normal"):
     unit = variant == "unit"
     sq = 1.0 if unit else 1.0 / np.sqrt(wl.Dqk)
     si = 1.0 if unit else 1.0 / np.sqrt(wl.Di)
-    q = np.zeros((n, wl.H, wl.Dqk), dtype=np.float32 if wl.attn_dtype == "f32" else np.uint16)
+    q = np.zeros((0 if indexer_only else n, wl.H, wl.Dqk), dtype=np.float32 if wl.attn_dtype == "f32" else np.uint16)
     fp8 = wl.idx_dtype == "fp8"
     qi = np.zeros((n, wl.Hi, wl.Di), dtype={"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}[wl.idx_dtype])
     w = np.zeros((n, wl.Hi), dtype=np.float32)
@@ -260,8 +261,9 @@ def query_inputs(wl: Workload, tokens, variant="normal"):
         if t < 0:
             continue
         row = int(kv_row[j])
-        g = _rng(wl.wid, T_Q, row, variant)
-        q[j] = _store(g.standard_normal((wl.H, wl.Dqk)) * sq, wl.attn_dtype)
+        if not indexer_only:
+            g = _rng(wl.wid, T_Q, row, variant)
+            q[j] = _store(g.standard_normal((wl.H, wl.Dqk)) * sq, wl.attn_dtype)
         g = _rng(wl.wid, T_QIDX, row, variant)
         if variant == "int":
             x = g.integers(-4, 5, size=(wl.Hi, wl.Di)).astype(np.float64)

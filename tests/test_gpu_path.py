@@ -51,9 +51,13 @@ def gpu_rank_path(wl, variant, dev, rank=None, keep_scores=False):
     torch.cuda.synchronize()
     res = dict(meta={k: (v.cpu().numpy() if v is not None else None) for k, v in meta.items()}, err=err.item(),
                idx=idx.cpu().numpy(), out=out, toks=toks, inp=inp, qin=qin, n_real=n_real, tpr=tpr)
-    if keep_scores:
-        ld = nbytes // 4 // max(n_real, 1)
-        res["scores"] = ws.view(torch.float32)[:n_real * ld].view(n_real, ld).cpu().numpy()
+    if keep_scores:  # full score rows from the two-stage entry point (the fused call may keep none)
+        vis = max_kv // wl.compress if wl.compress > 1 else max_kv
+        sc = torch.empty(max(n_real, 1), (vis + 63) // 64 * 64, dtype=torch.float32, device=dev)
+        D.indexer_scores(q_idx, w_d, k_d, meta["local_query_start_loc"], meta["local_seq_lens"], cu_kv, max_kv, sc,
+                         **{k: v for k, v in kw.items() if k not in ("window", "window_kv_start", "kv_row_base")})
+        torch.cuda.synchronize()
+        res["scores"] = sc[:n_real].cpu().numpy()
     return res
 
 
@@ -118,6 +122,17 @@ def test_path_integer_inputs_topk_exact(name, kw):
     res = gpu_rank_path(wl, "int", dev)
     n = res["n_real"]
     rows = range(n) if n <= 120 else np.unique(np.linspace(0, n - 1, 120).astype(int))
+    check_against_oracle(wl, "int", res, rows=rows)
+
+
+@pytest.mark.parametrize("name", ["long_131k_fp8", "chunk_inseq_cp8_last_8k_p56k"])
+def test_path_full_size_integer_inputs_sampled(name):
+    """Rows longer than 32768 keys take the candidate-list top-k; integer inputs make it exact."""
+    dev = gpu()
+    wl = S.WORKLOADS[name]
+    res = gpu_rank_path(wl, "int", dev)
+    n = res["n_real"]
+    rows = np.unique(np.concatenate([[0, 1, n - 2, n - 1], np.linspace(0, n - 1, 8).astype(int)]))
     check_against_oracle(wl, "int", res, rows=rows)
 
 

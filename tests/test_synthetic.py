@@ -55,3 +55,12 @@ def test_fp8_inputs_respect_the_range_and_scales():
 def test_var_batch_lengths_are_seeded():
     lens = S.WORKLOADS["rr_cp4_r1_var8_cmp4"].lens
     assert len(lens) == 8 and all(1024 <= l <= 16384 for l in lens)
+
+
+def test_indexer_only_query_inputs_draw_the_same_values():
+    wl = S.WORKLOADS["long_131k_fp8"].with_(lens=(300,))
+    a = S.query_inputs(wl, [0, 7, 299], indexer_only=True)
+    b = S.query_inputs(wl, [0, 7, 299])
+    assert a["q"].shape[0] == 0
+    for k in ("q_idx", "w", "q_scale"):
+        assert np.array_equal(a[k], b[k]), k
