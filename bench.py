@@ -263,7 +263,7 @@ def main():
                       "sparse_attn_frac": attn_flops / attn_s / 1e12 / attn_peak,
                       "indexer_frac": idx_flops / (indexer_ms * 1e-3) / 1e12 / idx_peak},
         "stages_ms": {**stage, "indexer": indexer_ms, "topk": topk_ms},
-        "indexer_topk_selection": "candidate lists" if vis_max > max(32768, wl.topk) else "score rows",
+        "indexer_topk_selection": "candidate lists" if vis_max > max(98304, wl.topk) else "score rows",
         "topk_hbm_frac": topk_bytes / (topk_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "work": {"indexer_pairs": pairs, "selected_rows": selected, "attn_gflop": attn_flops / 1e9,
                  "indexer_gflop": idx_flops / 1e9, "topk_mbytes": topk_bytes / 1e6},

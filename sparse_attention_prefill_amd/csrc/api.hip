@@ -48,26 +48,30 @@ int64_t score_ld(const dsa_indexer_topk_args* a) {
 }
 
 // Candidate mode (rows longer than max(kFuseMin, topk) are selected from lists of their best
-// scores, see topk.hip): only with the 64 x 128 matrix-core indexer.
+// scores, see topk.hip): only with the 64 x 128 matrix-core indexer, and only when some row is
+// longer than kFuseLaunch keys.
 bool candidate_mode(const dsa_indexer_topk_args* a) {
   const bool mfma = a->n_heads == 64 && a->head_dim == 128 && (a->dtype == DSA_BF16 || a->dtype == DSA_FP8_E4M3);
-  return mfma && max_visible(a) > std::max(kFuseMin, a->topk);
+  return mfma && max_visible(a) > std::max(kFuseLaunch, a->topk);
 }
 // Workspace of candidate mode: per row a 128 KB slot (a score row of kFuseMin floats, or a list
 // of kFuseCap entries), thresholds and list lengths, and the refill scratch rows.
 struct CandLayout {
-  size_t slots, theta, n_cand, scratch, total;
-  int n_scratch;
+  size_t slots, theta, n_cand, status, scratch, total;
+  int n_scratch, segs;
   int64_t sld;
 };
 CandLayout cand_layout(const dsa_indexer_topk_args* a) {
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   CandLayout L;
   const size_t nq = size_t(a->nq > 0 ? a->nq : 1);
+  int chunk_keys = 0;
+  L.segs = indexer_key_chunks(a, max_visible(a), &chunk_keys);
   L.slots = 0;
   L.theta = up(nq * size_t(kFuseCap) * sizeof(uint2));
   L.n_cand = L.theta + up(nq * sizeof(uint32_t));
-  L.scratch = L.n_cand + up(nq * sizeof(int32_t));
+  L.status = L.n_cand + up(nq * size_t(L.segs) * sizeof(int32_t));
+  L.scratch = L.status + up(nq * sizeof(int32_t));
   L.n_scratch = std::min(int(nq), kRefillBlocks);
   L.sld = score_ld(a);
   L.total = L.scratch + size_t(L.n_scratch) * size_t(L.sld) * sizeof(float);
@@ -198,8 +202,10 @@ dsa_status dsa_indexer_topk(const dsa_indexer_topk_args* a, void* stream) {
   cm.fuse_above = std::max(kFuseMin, a->topk);
   cm.theta = reinterpret_cast<uint32_t*>(ws + L.theta);
   cm.n_cand = reinterpret_cast<int32_t*>(ws + L.n_cand);
+  cm.status = reinterpret_cast<int32_t*>(ws + L.status);
   cm.cand = reinterpret_cast<uint2*>(ws + L.slots);
   cm.cap = kFuseCap;
+  cm.segs = L.segs;
   float* score_rows = reinterpret_cast<float*>(ws + L.slots);  // short rows: kFuseMin floats per slot
   st = launch_topk_theta(a, max_visible(a), cm, s);
   if (st != DSA_OK) return st;

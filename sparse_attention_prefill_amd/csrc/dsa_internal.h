@@ -98,11 +98,15 @@ __device__ inline bool query_view(const int32_t* __restrict__ cu_q, const int32_
 }
 
 // ---------------------------------------------------------------------------------------------
-// Indexer + top-k without score rows for long rows. A row with more than fuse_above visible keys
-// (fuse_above = max(kFuseMin, K)) is a candidate row: a sample of its scores sets a threshold,
-// the indexer appends only the scores at or above it to the row's list, and the top-k selects
-// from the list. Shorter rows keep score rows of kFuseMin floats in the same per-row slot.
+// Indexer + top-k without score rows for long rows. A launch whose longest row has more than
+// kFuseLaunch visible keys runs in candidate mode: there a row with more than fuse_above visible
+// keys (fuse_above = max(kFuseMin, K)) is a candidate row, a sample of its scores sets a
+// threshold, the indexer appends only the scores at or above it to the row's list, and the top-k
+// selects from the list. Shorter rows keep score rows of kFuseMin floats in the same per-row
+// slot. (The sample, the list select and the list appends cost about as much per row as reading
+// a 100K-key score row once, so shorter launches keep the score rows.)
 // ---------------------------------------------------------------------------------------------
+constexpr int kFuseLaunch = 98304;  // candidate mode when some row has more visible keys
 constexpr int kFuseMin = 32768;   // longest score row (keys) outside candidate mode
 constexpr int kFuseCap = 16384;   // list entries per row: 8 bytes each, the size of that score row
 constexpr int kRefillBlocks = 256;  // workgroups (and scratch rows) recomputing unusable lists
@@ -110,10 +114,15 @@ constexpr int kRefillBlocks = 256;  // workgroups (and scratch rows) recomputing
 struct CandidateMode {
   int fuse_above;     // rows with more visible keys are candidate rows
   uint32_t* theta;    // [nq] thresholds as order keys
-  int32_t* n_cand;    // [nq] list lengths (entries past cap are dropped but counted)
-  uint2* cand;        // [nq, cap] (score bits, position)
+  int32_t* n_cand;    // [nq, segs] entries found per list segment (past the segment's end: counted only)
+  int32_t* status;    // [nq] 1 when the row was selected from its list, 0 when it must be recomputed
+  uint2* cand;        // [nq, cap] (score bits, position): segs segments of cap / segs entries
   int cap;
+  int segs;           // list segments per row = grid.y of the indexer launch
 };
+
+// grid.y (key chunks per query group) of the 64 x 128 indexer launch, and its chunk length
+int indexer_key_chunks(const dsa_indexer_topk_args* a, int max_vis, int* chunk_keys);
 
 // Order-preserving 32-bit keys of float scores: -0.0 and +0.0 -> 0x80000000; a larger float
 // gives a larger key; finite floats stay above 2^23.

@@ -20,9 +20,9 @@
 //    the tile's k_scale values are staged into LDS by the same direct loads as the keys.
 //    Candidate mode (rows longer than the fused-selection bound): instead of writing a score
 //    row, a wave keeps only the scores at or above its row's threshold theta (a 32-bit order
-//    key, see topk.hip) and appends them, with their positions, to the row's candidate list:
-//    hits are staged in a per-wave LDS buffer and flushed with one global atomic that claims
-//    the list slots. The top-k then selects from the list, so no full score row is ever written.
+//    key, see topk.hip) and appends them, with their positions, to its own segment of the row's
+//    candidate list (one segment per grid.y slice, so no two workgroups share one and no atomics
+//    are needed). The top-k then selects from the segments: no full score row is written.
 //  * indexer_generic: float32 / bf16, small shapes (VALU, one thread per (query, key)).
 #include <algorithm>
 
@@ -76,7 +76,7 @@ __global__ __launch_bounds__(kGenThreads) void indexer_generic(
 // ---------------------------------------------------------------------------------------------
 constexpr int kHi = kIdxHeads, kDi = kIdxDim;
 constexpr int kWaves = 8, kThreads = kWaves * 64;
-constexpr int kStage = 256;  // candidate-mode LDS staging entries per wave
+
 constexpr int kKeyTile = 128;
 constexpr int kChunkKeys = 16 * kKeyTile;  // smallest key chunk per workgroup (grid.y splits longer ranges)
 constexpr int kTargetWorkgroups = 2048;    // chunks grow until the grid is about this large
@@ -89,21 +89,13 @@ struct IdxCfg {
   static constexpr int kLoads = kKeyTile * kChunks / kThreads;    // direct loads per lane per tile: 2 or 4
 };
 
-// Physical 16-byte chunk of logical chunk c of key row n in an LDS tile. 256-byte rows (bf16):
-// XOR with n & 15, so the 16 rows read together by one MFMA operand load hit 16 distinct bank
-// groups. 128-byte rows (fp8): a 3-bit XOR chosen so that rows n and n + 8 (which share banks)
-// also differ.
-template <int CHUNKS>
-__device__ inline int kswz(int n, int c) {
-  if constexpr (CHUNKS == 16) return c ^ (n & 15);
-  else return c ^ (((n >> 1) & 3) | (((n ^ (n >> 3)) & 1) << 2));
-}
-
 // bf16: one workgroup per CU (its 64 x 128 query operand takes 64 VGPRs per lane), with the
 // epilogue software-pipelined against the next block's MFMAs. fp8: two workgroups per CU
 // (4 waves per SIMD, at most 128 VGPRs), which hides more than the pipelining does.
 // Candidate mode (CAND): rows with more than fuse_above visible keys append their scores at or
-// above theta[i] to cand[i * cand_cap ...] (count in n_cand[i]); shorter rows write score rows.
+// above theta[i] to segment blockIdx.y of cand[i * cand_cap ...] (cand_cap / gridDim.y entries;
+// count in n_cand[i * gridDim.y + blockIdx.y], which the caller zeroes); shorter rows write score
+// rows.
 template <bool FP8, bool CAND>
 __global__ __launch_bounds__(kThreads, FP8 ? 4 : 1) void indexer_mfma(
     const unsigned char* __restrict__ qi, const float* __restrict__ q_scale, const float* __restrict__ w,
@@ -116,7 +108,6 @@ __global__ __launch_bounds__(kThreads, FP8 ? 4 : 1) void indexer_mfma(
   __shared__ __attribute__((aligned(16))) unsigned char tiles[2 * C::kTileBytes];
   __shared__ __attribute__((aligned(16))) float ks_tile[2][FP8 ? kKeyTile : 4];
   __shared__ int s_lo[kWaves], s_hi[kWaves];
-  __shared__ uint2 stage[CAND ? kWaves : 1][CAND ? kStage : 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave (known to the compiler)
@@ -161,19 +152,14 @@ __global__ __launch_bounds__(kThreads, FP8 ? 4 : 1) void indexer_mfma(
   float wv[2][16];  // weights of the 16 heads this lane holds per head block, in output layout
   if (ok) load_query_operands<FP8>(qi, w, q_scale, i, qa, wv);
 
-  // candidate mode: this wave's row keeps scores whose order key is >= theta_k
+  // Candidate mode: this wave's row keeps the scores whose order key is >= theta_k, appended to
+  // its own segment of the row's list (segment blockIdx.y of gridDim.y, seg_cap entries) with a
+  // register count; no atomics. The count is stored once at the end, overflow included.
   const bool cand_row = CAND && ok && hi - lo > fuse_above;  // wave-uniform
   const uint32_t theta_k = cand_row ? theta[i] : 0u;
-  int st_n = 0;  // entries staged in stage[wave] (wave-uniform)
-  auto flush = [&]() {
-    int base = 0;
-    if (lane == 0) base = atomicAdd(&n_cand[i], st_n);
-    base = __builtin_amdgcn_readfirstlane(base);
-    for (int j = lane; j < st_n; j += 64)
-      if (base + j < cand_cap) cand[int64_t(i) * cand_cap + base + j] = stage[wave][j];
-    st_n = 0;
-  };
-
+  const int seg_cap = cand_cap / int(gridDim.y);
+  uint2* seg = CAND ? cand + int64_t(i) * cand_cap + int64_t(blockIdx.y) * seg_cap : nullptr;
+  int st_n = 0;  // entries this wave found for its row (wave-uniform)
 #pragma unroll 1
   for (int64_t cs = int64_t(blockIdx.y) * chunk_keys; cs < int64_t(uhi) - ulo; cs += int64_t(gridDim.y) * chunk_keys) {
     const int glo = ulo + int(cs);
@@ -227,17 +213,7 @@ __global__ __launch_bounds__(kThreads, FP8 ? 4 : 1) void indexer_mfma(
         // epilogue, so the VALU epilogue runs under the matrix-core work
         auto block_mfma = [&](int nb, f32x16& a0, f32x16& a1) {
           const int n = 32 * nb + l32;
-          block_mfma_chains<FP8>(qa, [&](int ks) {
-            if constexpr (FP8) {
-              const int c0 = 4 * ks + 2 * half;  // two 16-byte chunks: d in [64ks + 32half, +32)
-              const i32x4 x0 = *reinterpret_cast<const i32x4*>(tb + n * C::kKeyBytes + kswz<C::kChunks>(n, c0) * 16);
-              const i32x4 x1 = *reinterpret_cast<const i32x4*>(tb + n * C::kKeyBytes + kswz<C::kChunks>(n, c0 + 1) * 16);
-              return i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-            } else {
-              const int c = 2 * ks + half;
-              return *reinterpret_cast<const bf16x8*>(tb + n * C::kKeyBytes + kswz<C::kChunks>(n, c) * 16);
-            }
-          }, a0, a1);
+          block_mfma_chains<FP8>(qa, [&](int ks) { return key_operand_lds<FP8>(tb, n, ks); }, a0, a1);
         };
         // lane holds key 32nb + l32 and heads 32m + 8(r/4) + 4half + r%4
         auto block_epilogue = [&](int nb, const f32x16& a0, const f32x16& a1) {
@@ -250,9 +226,9 @@ __global__ __launch_bounds__(kThreads, FP8 ? 4 : 1) void indexer_mfma(
             const bool hit = in && order_key(sacc) >= theta_k;
             const uint64_t m = ballot(hit);
             if (m) {
-              if (hit) stage[wave][st_n + lanes_below(m)] = make_uint2(__float_as_uint(sacc), uint32_t(key - q_origin));
+              const int slot = st_n + lanes_below(m);
+              if (hit && slot < seg_cap) seg[slot] = make_uint2(__float_as_uint(sacc), uint32_t(key - q_origin));
               st_n += __popcll(m);
-              if (st_n > kStage - 32) flush();
             }
           } else if (in) {
             if constexpr (FP8) sacc *= ks_tile[buf][32 * nb + l32];
@@ -279,22 +255,29 @@ __global__ __launch_bounds__(kThreads, FP8 ? 4 : 1) void indexer_mfma(
       DSA_TILE_BARRIER_LDS();
     }
   }
-  if (CAND && cand_row && st_n > 0) flush();
+  if (CAND && cand_row && lane == 0) n_cand[int64_t(i) * gridDim.y + blockIdx.y] = st_n;
 }
 
 }  // namespace
+
+// Chunks of 2048 keys fill the GPU for short query batches; long batches take larger chunks
+// (fewer reloads of each group's query block, fewer workgroup start-ups).
+int indexer_key_chunks(const dsa_indexer_topk_args* a, int max_vis, int* chunk_keys) {
+  const int64_t groups = (a->nq + kWaves - 1) / kWaves, base_chunks = (max_vis + kChunkKeys - 1) / kChunkKeys;
+  const int64_t merge = std::max<int64_t>(1, groups * base_chunks / kTargetWorkgroups);
+  *chunk_keys = int(std::min<int64_t>(merge, base_chunks) * kChunkKeys);
+  return std::max(1, (max_vis + *chunk_keys - 1) / *chunk_keys);
+}
 
 dsa_status launch_indexer_scores(const dsa_indexer_topk_args* a, float* scores, int64_t ld, int max_vis,
                                  int skip_le, const CandidateMode* cm, hipStream_t stream) {
   if (a->nq == 0 || max_vis <= skip_le) return DSA_OK;
   const int stride = a->q_stride, ratio = a->compress_ratio;
   if (a->n_heads == kHi && a->head_dim == kDi && (a->dtype == DSA_BF16 || a->dtype == DSA_FP8_E4M3)) {
-    // chunks of 2048 keys fill the GPU for short query batches; long batches take larger chunks
-    // (fewer reloads of each group's query block, fewer workgroup start-ups)
-    const int64_t groups = (a->nq + kWaves - 1) / kWaves, base_chunks = (max_vis + kChunkKeys - 1) / kChunkKeys;
-    const int64_t merge = std::max<int64_t>(1, groups * base_chunks / kTargetWorkgroups);
-    const int chunk_keys = int(std::min<int64_t>(merge, base_chunks) * kChunkKeys);
-    const dim3 grid(unsigned(groups), unsigned((max_vis + chunk_keys - 1) / chunk_keys));
+    int chunk_keys = 0;
+    const int gy = indexer_key_chunks(a, max_vis, &chunk_keys);
+    const dim3 grid(unsigned((a->nq + kWaves - 1) / kWaves), unsigned(gy));
+    if (cm && cm->segs != gy) return fail(DSA_ERR_INVALID_ARG, "indexer: candidate segments do not match the grid");
     const CandidateMode none{INT32_MAX, nullptr, nullptr, nullptr, 0};
     const CandidateMode& c = cm ? *cm : none;
 #define DSA_IDX_ARGS                                                                                           \

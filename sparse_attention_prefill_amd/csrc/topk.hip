@@ -737,24 +737,54 @@ constexpr int kCandEPT = kFuseCap / kCandNT;           // 16 list entries per th
 
 // Threshold of each candidate row (one wave per row, 8 rows per workgroup): the scores of 16
 // tiles of 128 consecutive keys spread evenly over the row, and theta = the 22-bit key prefix of
-// the sample's r-th largest score, r = ceil(3 K * 2048 / ev): about 3K of the row's keys reach
-// theta, K of them needed, the list holding kFuseCap. Also zeroes every row's list count.
+// the sample's r-th largest score. With m = 2048 sampled of ev keys, the keys reaching the r-th
+// sample number about r * ev / m with a spread of about sqrt(r) * ev / m; r is the smallest
+// rank whose count stays 5.5 spreads above K, so a list falls short of K very rarely (those rows
+// are recomputed) while holding about K + 5.5 sqrt(K ev / m) ev / m entries. When the 8 rows of
+// the workgroup are candidate rows of one request they share the sample positions (those of the
+// shortest row) and each tile is staged once in LDS; otherwise each wave reads its own keys.
+// Also zeroes every row's list-segment counts.
 template <bool FP8>
 __global__ __launch_bounds__(512) void topk_theta_kernel(
     const unsigned char* __restrict__ qi, const float* __restrict__ q_scale, const float* __restrict__ w,
     const unsigned char* __restrict__ ki, const float* __restrict__ k_scale, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ used_kv, const int32_t* __restrict__ cu_kv, int batch, int stride, int ratio, int nq,
-    int nk, int max_vis, int K, int fuse_above, uint32_t* __restrict__ theta, int32_t* __restrict__ n_cand) {
+    int nk, int max_vis, int K, int fuse_above, uint32_t* __restrict__ theta, int32_t* __restrict__ n_cand,
+    int segs) {
+  constexpr int kBytes = IdxOps<FP8>::kKeyBytes, kChunks = kBytes / 16;
   __shared__ alignas(16) uint32_t hist[8][kThetaBins];
-  const int lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  __shared__ alignas(16) unsigned char tile[128 * kBytes];
+  __shared__ int s_kv0[8], s_ev[8];
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int i = blockIdx.x * 8 + wave;
-  if (i >= nq) return;  // no workgroup barrier below
-  if (lane == 0) n_cand[i] = 0;
-  QueryView v;
-  if (!query_view(cu_q, used_kv, cu_kv, batch, stride, i, &v)) return;
-  const int ev = ratio > 1 ? v.E / ratio : v.E;
-  if (v.E < 1 || ev <= fuse_above || ev > max_vis || v.kv0 < 0 || int64_t(v.kv0) + ev > nk) return;
+  bool cand = false;
+  int kv0 = 0, ev = 0;
+  if (i < nq) {
+    for (int y = lane; y < segs; y += 64) n_cand[int64_t(i) * segs + y] = 0;
+    QueryView v;
+    if (query_view(cu_q, used_kv, cu_kv, batch, stride, i, &v)) {
+      ev = ratio > 1 ? v.E / ratio : v.E;
+      kv0 = v.kv0;
+      cand = v.E >= 1 && ev > fuse_above && ev <= max_vis && v.kv0 >= 0 && int64_t(v.kv0) + ev <= nk;
+    }
+  }
+  if (lane == 0) {
+    s_kv0[wave] = cand ? kv0 : -1;
+    s_ev[wave] = cand ? ev : 0;
+  }
+  __syncthreads();
+  bool shared = true;
+  int ev_s = INT32_MAX;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    shared = shared && s_kv0[k] >= 0 && s_kv0[k] == s_kv0[0];
+    ev_s = min(ev_s, s_ev[k]);
+  }
+  if (!shared) {
+    if (!cand) return;  // no workgroup barrier on this path
+    ev_s = ev;
+  }
 
   typename IdxOps<FP8>::AOp qa[2][IdxOps<FP8>::kKsteps];
   float wv[2][16];
@@ -763,17 +793,40 @@ __global__ __launch_bounds__(512) void topk_theta_kernel(
   // the keys of block 2p + h
   uint32_t sk[kSampleKeys / 64];
 #pragma unroll 1
-  for (int p = 0; p < kSampleKeys / 64; ++p) {
-    float sc[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int b = 2 * p + h, tile = b >> 2;
-      const int start = int(int64_t(tile) * (ev - 128) / (kSampleTiles - 1));
-      sc[h] = key_score_global<FP8>(qa, wv, ki, k_scale, v.kv0 + start + 32 * (b & 3) + l32);
+  for (int tl = 0; tl < kSampleTiles; ++tl) {
+    const int start = int(int64_t(tl) * (ev_s - 128) / (kSampleTiles - 1));
+    if (shared) {
+      __syncthreads();  // the previous tile is consumed
+      for (int f = tid; f < 128 * kChunks; f += 512) {
+        const int n = f / kChunks, c = f - n * kChunks;
+        *reinterpret_cast<i32x4*>(tile + n * kBytes + kswz<kChunks>(n, c) * 16) =
+            *reinterpret_cast<const i32x4*>(ki + int64_t(kv0 + start + n) * kBytes + c * 16);
+      }
+      __syncthreads();
     }
-    sk[p] = order_key(half ? sc[1] : sc[0]);
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp) {
+      float sc[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int n = 32 * (2 * pp + h) + l32;  // row in the tile
+        const int row = kv0 + start + n;
+        f32x16 a0, a1;
+        if (shared) block_mfma_chains<FP8>(qa, [&](int ks) { return key_operand_lds<FP8>(tile, n, ks); }, a0, a1);
+        else block_mfma_chains<FP8>(qa, [&](int ks) { return key_operand_global<FP8>(ki, row, ks); }, a0, a1);
+        float x = block_head_sum(wv, a0, a1);
+        if constexpr (FP8) x *= k_scale[row];
+        sc[h] = x + 0.f;
+      }
+      sk[2 * tl + pp] = order_key(half ? sc[1] : sc[0]);
+    }
   }
-  const int r_s = int(min<int64_t>(kSampleKeys, (int64_t(3) * K * kSampleKeys + ev - 1) / ev));
+  if (!cand) return;  // shared path: every wave is a candidate row; kept for clarity
+
+  // r: smallest rank with r * ev / m - 5.5 sqrt(r) * ev / m >= K
+  const double km = double(K) * kSampleKeys / ev;
+  const double sr = 2.75 + sqrt(2.75 * 2.75 + km);
+  const int r_s = int(min(double(kSampleKeys), ceil(sr * sr)));
   uint32_t* h = hist[wave];
   int bin1, bin2, rem, cnt;
   for (int b = 4 * lane; b < kThetaBins; b += 256) *reinterpret_cast<uint4*>(h + b) = uint4{0, 0, 0, 0};
@@ -800,19 +853,23 @@ struct CandShared {
   } u;
   alignas(16) uint32_t hist_r[kBinsR];
   int scan[2 * (kCandNT / 64 + 1)];
+  int seg_n[64];  // list-segment counts
   uint32_t prefix;
   int remaining;
 };
 
-// Exact top-K of a candidate row from its list (every key >= theta, with its position): the
-// three-digit radix select over the list in registers, then ids from position bitmaps. A row
-// whose list holds fewer than K entries or overflowed is left to topk_refill_kernel.
+// Exact top-K of a candidate row from its list (every key >= theta, with its position). The
+// list keys are taken relative to theta, d = key - theta: the first digit is the 12 bits of d
+// below its highest set bit across the list, so even a list packed into a few float exponents
+// spreads over the 4096-bin histogram; the lower bits follow in digits of at most 10 bits. The
+// ids are then emitted from position bitmaps. A row whose list holds fewer than K entries or
+// overflowed is left to topk_refill_kernel.
 __global__ __launch_bounds__(kCandNT, 2) void topk_cand_kernel(
-    const uint2* __restrict__ cand, const int32_t* __restrict__ n_cand, int cap, int fuse_above,
-    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ used_kv, const int32_t* __restrict__ cu_kv,
-    const int32_t* __restrict__ win_kv, int batch, int stride, int ratio, int max_vis, int K, int window,
-    int kv_row_base, int32_t* __restrict__ out, int32_t* __restrict__ err_flag) {
-  constexpr int NT = kCandNT;
+    const uint2* __restrict__ cand, const int32_t* __restrict__ n_cand, int32_t* __restrict__ status,
+    const uint32_t* __restrict__ theta, int cap, int segs, int fuse_above, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ used_kv,
+    const int32_t* __restrict__ cu_kv, const int32_t* __restrict__ win_kv, int batch, int stride, int ratio,
+    int max_vis, int K, int window, int kv_row_base, int32_t* __restrict__ out, int32_t* __restrict__ err_flag) {
+  constexpr int NT = kCandNT, NW = NT / 64;
   __shared__ CandShared sh;
   const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -825,56 +882,82 @@ __global__ __launch_bounds__(kCandNT, 2) void topk_cand_kernel(
   if (!row_setup<NT>(cu_q, used_kv, cu_kv, win_kv, batch, stride, ratio, max_vis, kMaxRow, K, window, kv_row_base,
                      orow, err_flag, &ri))
     return;
-  const int n = n_cand[row];
-  if (n < K || n > cap) return;
+  // the list: segment y holds its first min(count_y, seg_cap) slots; a segment that overflowed
+  // or a list shorter than K sends the row to the recompute
+  const int seg_cap = cap / segs;
+  if (tid < segs) sh.seg_n[tid] = n_cand[int64_t(row) * segs + tid];
+  __syncthreads();
+  int n = 0;
+  bool usable = true;
+  for (int y = 0; y < segs; ++y) {
+    n += sh.seg_n[y];
+    usable = usable && sh.seg_n[y] <= seg_cap;
+  }
+  usable = usable && n >= K;
+  if (tid == 0) status[row] = usable ? 1 : 0;
+  if (!usable) return;
 
   const uint2* crow = cand + int64_t(row) * cap;
-  uint32_t keys[kCandEPT];
+  const uint32_t th = theta[row];
+  uint32_t d[kCandEPT];
   int pos[kCandEPT];
+  uint32_t mx = 0;
 #pragma unroll
   for (int j = 0; j < kCandEPT; ++j) {
-    const int c = j * NT + tid;
-    const uint2 e = c < n ? crow[c] : uint2{0u, 0u};
-    keys[j] = order_key_bits(e.x);
-    pos[j] = c < n ? int(e.y) : -1;
+    const int c = j * NT + tid, y = c / seg_cap;
+    const bool valid = y < segs && c - y * seg_cap < sh.seg_n[min(y, segs - 1)];
+    const uint2 e = valid ? crow[c] : uint2{0u, 0u};
+    pos[j] = valid ? int(e.y) : -1;
+    d[j] = valid ? order_key_bits(e.x) - th : 0u;
+    mx = max(mx, d[j]);
   }
-  // digit 1
+  // highest set bit of d over the list -> shift of the first digit
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mx = max(mx, uint32_t(__shfl_xor(int(mx), o, 64)));
+  if (lane == 0) sh.scan[wave] = int(mx);
   zero_words<NT>(sh.u.hist, kBins0);
   __syncthreads();
+  uint32_t mall = 0;
+#pragma unroll
+  for (int k = 0; k < NW; ++k) mall = max(mall, uint32_t(sh.scan[k]));
+  const int s1 = max(0, 32 - int(__builtin_clz(mall | 1u)) - 12);  // d >> s1 < 4096
 #pragma unroll
   for (int j = 0; j < kCandEPT; ++j)
-    if (pos[j] >= 0) atomicAdd(&sh.u.hist[keys[j] >> 20], 1u);
+    if (pos[j] >= 0) atomicAdd(&sh.u.hist[d[j] >> s1], 1u);
   __syncthreads();
   if (wave == 0) {
     int bin, rem, cnt;
     wave_select<kBins0>(sh.u.hist, K, &bin, &rem, &cnt);
     if (lane == 0) {
-      sh.prefix = uint32_t(bin) << 20;
+      sh.prefix = uint32_t(bin);
       sh.remaining = rem;
     }
   }
-  // digits 2 and 3 over the registers
+  // lower digits: bits [lo, lo + wb) among the keys whose bits above match the prefix
+  int lo = s1;
 #pragma unroll 1
-  for (int r = 0; r < 2; ++r) {
-    const int shift = 10 - 10 * r;
+  while (lo > 0) {
+    const int wb = min(10, lo);
+    lo -= wb;
     zero_words<NT>(sh.hist_r, kBinsR);
     __syncthreads();
-    const uint32_t pfx = sh.prefix >> (shift + 10);
+    const uint32_t pfx = sh.prefix;
 #pragma unroll
     for (int j = 0; j < kCandEPT; ++j)
-      if (pos[j] >= 0 && (keys[j] >> (shift + 10)) == pfx) atomicAdd(&sh.hist_r[(keys[j] >> shift) & (kBinsR - 1)], 1u);
+      if (pos[j] >= 0 && (d[j] >> (lo + wb)) == pfx) atomicAdd(&sh.hist_r[(d[j] >> lo) & ((1u << wb) - 1u)], 1u);
     __syncthreads();
     if (wave == 0) {
       int bin, rem, cnt;
       wave_select<kBinsR>(sh.hist_r, sh.remaining, &bin, &rem, &cnt);
       if (lane == 0) {
-        sh.prefix |= uint32_t(bin) << shift;
+        sh.prefix = (pfx << wb) | uint32_t(bin);
         sh.remaining = rem;
       }
     }
-    __syncthreads();
+    __syncthreads();  // the select has read hist_r before the next digit clears it
   }
-  const uint32_t tau = sh.prefix;
+  __syncthreads();
+  const uint32_t tau = sh.prefix;  // relative to theta
   const int need = sh.remaining;
   const int n_chunks = (ev + 63) >> 6;
   uint64_t* gt = sh.u.bits[0];
@@ -884,14 +967,14 @@ __global__ __launch_bounds__(kCandNT, 2) void topk_cand_kernel(
 #pragma unroll
   for (int j = 0; j < kCandEPT; ++j) {
     if (pos[j] < 0) continue;
-    if (keys[j] > tau) atomicOr(&gt[pos[j] >> 6], 1ull << (pos[j] & 63));
-    else if (keys[j] == tau) atomicOr(&eq[pos[j] >> 6], 1ull << (pos[j] & 63));
+    if (d[j] > tau) atomicOr(&gt[pos[j] >> 6], 1ull << (pos[j] & 63));
+    else if (d[j] == tau) atomicOr(&eq[pos[j] >> 6], 1ull << (pos[j] & 63));
   }
   __syncthreads();
   emit_from_bitmaps<NT>(gt, eq, n_chunks, need, K, ri.base, orow, sh.scan);
 }
 
-// Candidate rows whose list fell short of K or overflowed: a persistent workgroup recomputes
+// Candidate rows whose list was unusable (status 0): a persistent workgroup recomputes
 // each such row's scores (the same arithmetic as the indexer) into its own scratch row and
 // selects from it like topk_stream_kernel. Rows whose list was usable are skipped.
 template <bool FP8>
@@ -899,8 +982,8 @@ __global__ __launch_bounds__(kStreamNT, 1) void topk_refill_kernel(
     const unsigned char* __restrict__ qi, const float* __restrict__ q_scale, const float* __restrict__ w,
     const unsigned char* __restrict__ ki, const float* __restrict__ k_scale, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ used_kv, const int32_t* __restrict__ cu_kv, int batch, int stride, int ratio, int nq,
-    int nk, int max_vis, int K, int window, int kv_row_base, int fuse_above, const int32_t* __restrict__ n_cand,
-    int cap, float* __restrict__ scratch, int64_t sld, int32_t* __restrict__ out) {
+    int nk, int max_vis, int K, int window, int kv_row_base, int fuse_above, const int32_t* __restrict__ status,
+    float* __restrict__ scratch, int64_t sld, int32_t* __restrict__ out) {
   __shared__ StreamShared sh;
   const int lane = threadIdx.x & 63, l32 = lane & 31, half = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -911,8 +994,7 @@ __global__ __launch_bounds__(kStreamNT, 1) void topk_refill_kernel(
     if (!query_view(cu_q, used_kv, cu_kv, batch, stride, row, &v)) continue;
     const int ev = ratio > 1 ? v.E / ratio : v.E;
     if (v.E < 1 || ev <= fuse_above || ev > max_vis || v.kv0 < 0 || int64_t(v.kv0) + ev > nk) continue;
-    const int n = n_cand[row];
-    if (n >= K && n <= cap) continue;
+    if (status[row] != 0) continue;
     typename IdxOps<FP8>::AOp qa[2][IdxOps<FP8>::kKsteps];
     float wv[2][16];
     load_query_operands<FP8>(qi, w, q_scale, row, qa, wv);
@@ -958,7 +1040,7 @@ dsa_status launch_topk_theta(const dsa_indexer_topk_args* a, int max_vis, const 
 #define DSA_THETA_ARGS                                                                                        \
   static_cast<const unsigned char*>(a->q_idx), a->q_scale, a->weights, static_cast<const unsigned char*>(a->k_idx), \
       a->k_scale, a->cu_seqlens_q, a->seqused_kv, a->cu_seqlens_kv, a->batch, a->q_stride, a->compress_ratio, a->nq, \
-      a->nk, max_vis, a->topk, cm.fuse_above, cm.theta, cm.n_cand
+      a->nk, max_vis, a->topk, cm.fuse_above, cm.theta, cm.n_cand, cm.segs
   if (a->dtype == DSA_FP8_E4M3) hipLaunchKernelGGL(topk_theta_kernel<true>, grid, dim3(512), 0, stream, DSA_THETA_ARGS);
   else hipLaunchKernelGGL(topk_theta_kernel<false>, grid, dim3(512), 0, stream, DSA_THETA_ARGS);
 #undef DSA_THETA_ARGS
@@ -976,7 +1058,8 @@ dsa_status launch_topk_candidates(const dsa_indexer_topk_args* a, const float* s
                      max_vis, a->topk, a->window, a->kv_row_base, a->topk_idx, a->err_flag, cm.fuse_above);
   dsa_status st = check_launch("topk_reg_kernel");
   if (st != DSA_OK) return st;
-  hipLaunchKernelGGL(topk_cand_kernel, grid, dim3(kCandNT), 0, stream, cm.cand, cm.n_cand, cm.cap, cm.fuse_above,
+  hipLaunchKernelGGL(topk_cand_kernel, grid, dim3(kCandNT), 0, stream, cm.cand, cm.n_cand, cm.status, cm.theta,
+                     cm.cap, cm.segs, cm.fuse_above,
                      a->cu_seqlens_q, a->seqused_kv, a->cu_seqlens_kv, a->window_kv_start, a->batch, a->q_stride,
                      a->compress_ratio, max_vis, a->topk, a->window, a->kv_row_base, a->topk_idx, a->err_flag);
   st = check_launch("topk_cand_kernel");
@@ -984,7 +1067,7 @@ dsa_status launch_topk_candidates(const dsa_indexer_topk_args* a, const float* s
 #define DSA_REFILL_ARGS                                                                                       \
   static_cast<const unsigned char*>(a->q_idx), a->q_scale, a->weights, static_cast<const unsigned char*>(a->k_idx), \
       a->k_scale, a->cu_seqlens_q, a->seqused_kv, a->cu_seqlens_kv, a->batch, a->q_stride, a->compress_ratio, a->nq, \
-      a->nk, max_vis, a->topk, a->window, a->kv_row_base, cm.fuse_above, cm.n_cand, cm.cap, scratch, sld, a->topk_idx
+      a->nk, max_vis, a->topk, a->window, a->kv_row_base, cm.fuse_above, cm.status, scratch, sld, a->topk_idx
   const dim3 rgrid(n_scratch);
   if (a->dtype == DSA_FP8_E4M3) hipLaunchKernelGGL(topk_refill_kernel<true>, rgrid, dim3(kStreamNT), 0, stream, DSA_REFILL_ARGS);
   else hipLaunchKernelGGL(topk_refill_kernel<false>, rgrid, dim3(kStreamNT), 0, stream, DSA_REFILL_ARGS);

@@ -1,8 +1,9 @@
 """GPU: indexer + top-k in candidate mode against the two-stage path, bit for bit.
 
-Rows with more than max(32768, K) visible keys are selected from lists of their best scores
-(a sampled threshold decides what the indexer keeps) instead of from full score rows; a row
-whose list falls short of K or overflows is recomputed and selected from a full row. Either
+In a launch whose longest row has more than 98304 visible keys, rows with more than
+max(32768, K) visible keys are selected from lists of their best scores (a sampled threshold
+decides what the indexer keeps) instead of from full score rows; a row whose list falls short
+of K or overflows is recomputed and selected from a full row. Either
 way the ids must be exactly those of dsa_topk_from_scores over dsa_indexer_scores, which are
 checked against the oracle elsewhere. Cases: long rows in bf16 and fp8, short and long rows in
 one batch, several requests in round-robin order, compressed keys with a window, and inputs
@@ -56,13 +57,15 @@ def _both(wl, variant, dev, zero_keys=False):
 
 
 CASES = [
-    ("inseq_cp8_last_8k", {"lens": (40000,)}, "normal"),
-    ("inseq_cp8_last_8k", {"lens": (40000,)}, "int"),
+    ("inseq_cp8_last_8k", {"lens": (100000,)}, "normal"),
+    ("inseq_cp8_last_8k", {"lens": (100000,)}, "int"),
     ("long_131k_fp8", {}, "normal"),
-    ("long_131k_fp8", {"lens": (45000,), "cp": 1, "rank": 0}, "normal"),     # short and long rows
-    ("rr_cp8_r3_batch4", {"lens": (50000, 36000, 5), "cp": 4, "rank": 1}, "normal"),
-    ("chunk_inseq_cp8_last_8k_p56k", {}, "normal"),
-    ("rr_cp4_r1_var8_cmp4", {"lens": (140000,), "cp": 4, "rank": 3}, "normal"),  # x4 keys, window
+    # short and long rows in one batch: request 1 rows stay under 32768 keys
+    ("long_131k_fp8", {"lens": (100000, 20000), "cp": 4, "rank": 3, "mode": "round_robin"}, "normal"),
+    ("rr_cp8_r3_batch4", {"lens": (110000, 36000, 5), "cp": 4, "rank": 1}, "normal"),
+    ("chunk_inseq_cp8_last_8k_p56k", {"prefix": (100000,)}, "normal"),
+    # x4 keys (visible = extent / 4) with a window; short and long rows
+    ("rr_cp4_r1_var8_cmp4", {"lens": (420000,), "cp": 16, "rank": 5}, "normal"),
 ]
 
 
@@ -70,14 +73,14 @@ CASES = [
 def test_candidate_lists_match_score_rows(name, kw, variant):
     dev = gpu()
     fused, ref, vis = _both(S.WORKLOADS[name].with_(**kw), variant, dev)
-    assert vis > 32768
+    assert vis > 98304
     assert np.array_equal(fused, ref)
 
 
 @pytest.mark.parametrize("name,kw,zero", [
-    ("inseq_cp8_last_8k", {"lens": (40000,), "topk": 16000}, False),   # lists overflow: every row recomputed
-    ("inseq_cp8_last_8k", {"lens": (40000,)}, True),                    # every score 0.0: ties at the cut
-    ("inseq_cp8_last_8k", {"lens": (45000,), "cp": 2, "rank": 1, "topk": 40000}, False),  # K above 32768
+    ("inseq_cp8_last_8k", {"lens": (100000,), "topk": 16000}, False),   # lists overflow: every row recomputed
+    ("inseq_cp8_last_8k", {"lens": (100000,)}, True),                    # every score 0.0: ties at the cut
+    ("inseq_cp8_last_8k", {"lens": (100000,), "cp": 4, "rank": 3, "topk": 40000}, False),  # K above 32768
 ])
 def test_recomputed_rows_match_score_rows(name, kw, zero):
     dev = gpu()
