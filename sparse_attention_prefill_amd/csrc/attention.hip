@@ -481,7 +481,8 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
     const int hl = 8 * (v >> 2) + 4 * half + (v & 3);
     const float iv = __shfl(inv, hl, 64);
 #pragma unroll
-    for (int db = 0; db < kDv / 32; ++db) op[hl * kDv + 32 * db + l32] = float_to_bf16_bits(oacc[db][v] * iv);
+    for (int db = 0; db < kDv / 32; ++db)  // round to nearest even (the hardware conversion)
+      op[hl * kDv + 32 * db + l32] = __builtin_bit_cast(uint16_t, (__bf16)(oacc[db][v] * iv));
   }
   if (lse && half == 0) lse[int64_t(i) * kH + h] = l_run > 0.f ? (m_used + log2f(l_run)) / kLog2e : -INFINITY;
 }

@@ -9,7 +9,7 @@
 // Kernels:
 //  * indexer_mfma<bf16|fp8>: 64 heads x 128. A workgroup of 8 waves owns 8 consecutive local
 //    queries (one per wave, whose 64 x 128 query block stays in VGPRs as the MFMA A operand)
-//    and sweeps 128-key tiles of one 2048-key chunk (grid.y) of the union of their causal key
+//    and sweeps 256-key tiles of one 2048-key chunk (grid.y) of the union of their causal key
 //    ranges, so even short query batches fill the GPU; tiles are staged in LDS
 //    with direct global->LDS loads (double buffered) and shared by the 8 waves. Each wave
 //    computes the 64 heads x 64 keys logits on 32x32 MFMAs (bf16 32x32x16, or fp8 32x32x64),
@@ -77,16 +77,17 @@ __global__ __launch_bounds__(kGenThreads) void indexer_generic(
 constexpr int kHi = kIdxHeads, kDi = kIdxDim;
 constexpr int kWaves = 8, kThreads = kWaves * 64;
 
-constexpr int kKeyTile = 128;
-constexpr int kChunkKeys = 16 * kKeyTile;  // smallest key chunk per workgroup (grid.y splits longer ranges)
+constexpr int kKeyTile = 256;     // keys per LDS tile (one barrier per tile)
+constexpr int kChunkKeys = 2048;  // smallest key chunk per workgroup (grid.y splits longer ranges)
 constexpr int kTargetWorkgroups = 2048;    // chunks grow until the grid is about this large
 
 template <bool FP8>
 struct IdxCfg {
   static constexpr int kKeyBytes = FP8 ? kDi : kDi * 2;          // 128 or 256
   static constexpr int kChunks = kKeyBytes / 16;                  // 8 or 16
-  static constexpr int kTileBytes = kKeyTile * kKeyBytes;         // 8 or 16 KiB
-  static constexpr int kLoads = kKeyTile * kChunks / kThreads;    // direct loads per lane per tile: 2 or 4
+  static constexpr int kTileBytes = kKeyTile * kKeyBytes;         // 32 or 64 KiB
+  static constexpr int kLoads = kKeyTile * kChunks / kThreads;    // direct loads per lane per tile: 4 or 8
+  static constexpr int kInFlight = kLoads + (FP8 ? 1 : 0);        // the next tile's loads (fp8: + its scales)
 };
 
 // bf16: one workgroup per CU (its 64 x 128 query operand takes 64 VGPRs per lane), with the
@@ -184,12 +185,14 @@ __global__ __launch_bounds__(kThreads, FP8 ? 4 : 1) void indexer_mfma(
     };
 
     // fp8: the tile's per-key scales are staged next to it in LDS: wave w copies keys
-    // [16w, 16w + 16) with one more direct load (16 active lanes of 4 bytes)
+    // [32w, 32w + 32) with one more direct load (32 active lanes of 4 bytes)
     auto issue_kscale = [&](int t, int buf) {
       if constexpr (FP8) {
-        if (lane < 16) {
-          const int key = glo + t * kKeyTile + 16 * wave + lane;
-          lds_dma4_v(k_scale + (key < nk ? key : nk - 1), __builtin_amdgcn_readfirstlane(lds_offset(ks_tile[buf] + 16 * wave)));
+        constexpr int kPerWave = kKeyTile / kWaves;  // scales each wave stages
+        if (lane < kPerWave) {
+          const int key = glo + t * kKeyTile + kPerWave * wave + lane;
+          lds_dma4_v(k_scale + (key < nk ? key : nk - 1),
+                     __builtin_amdgcn_readfirstlane(lds_offset(ks_tile[buf] + kPerWave * wave)));
         }
       }
     };
@@ -201,8 +204,11 @@ __global__ __launch_bounds__(kThreads, FP8 ? 4 : 1) void indexer_mfma(
         issue_kscale(t + 1, buf ^ 1);
         issue_tile(t + 1, buf ^ 1);
         // the next tile's loads (and its scales for fp8) may stay in flight
-        if constexpr (FP8) DSA_TILE_BARRIER_VMCNT(3);
-        else DSA_TILE_BARRIER_VMCNT(4);
+        if constexpr (C::kInFlight == 3) DSA_TILE_BARRIER_VMCNT(3);
+        else if constexpr (C::kInFlight == 4) DSA_TILE_BARRIER_VMCNT(4);
+        else if constexpr (C::kInFlight == 5) DSA_TILE_BARRIER_VMCNT(5);
+        else if constexpr (C::kInFlight == 8) DSA_TILE_BARRIER_VMCNT(8);
+        else static_assert(C::kInFlight == 3, "no barrier for this tile size");
       } else {
         DSA_TILE_BARRIER_VMCNT(0);
       }
