@@ -79,3 +79,26 @@ def test_missing_library_fails_loudly(monkeypatch):
     monkeypatch.setattr(B, "library_path", "/nonexistent/libdsa.so")
     with pytest.raises(B.DsaError):
         B.lib()
+
+
+def test_indexer_workspace_sizes_follow_the_selection_mode():
+    """Host-only sizing: score rows up to 98304 visible keys; above that (64 x 128 bf16/fp8 indexer)
+    one 128 KB list slot per row plus thresholds, segment counts, row status and 256 scratch rows."""
+    import torch
+    import sparse_attention_prefill_amd as D
+    nq = 1000
+    qi = torch.zeros(nq, 64, 128, dtype=torch.bfloat16)
+    w = torch.zeros(nq, 64)
+    ki = torch.zeros(200000, 128, dtype=torch.bfloat16)
+    cu_q = torch.tensor([0, nq], dtype=torch.int32)
+    used = torch.tensor([98304], dtype=torch.int32)
+    cu_kv = torch.tensor([0, 200000], dtype=torch.int32)
+    rows = D.indexer_topk_workspace(qi, w, ki, cu_q, used, cu_kv, 98304, topk=2048)
+    assert rows == nq * 98304 * 4
+    lists = D.indexer_topk_workspace(qi, w, ki, cu_q, used, cu_kv, 98305, topk=2048)
+    ld = (98305 + 63) // 64 * 64
+    assert nq * 131072 + nq * 4 * 3 + 256 * ld * 4 <= lists <= nq * 131072 + nq * 4 * (2 + 64) + 256 * ld * 4 + 1024
+    # a K above the launch bound keeps score rows; so does the generic (non 64 x 128) indexer
+    assert D.indexer_topk_workspace(qi, w, ki, cu_q, used, cu_kv, 100000, topk=100000) == nq * 100032 * 4
+    qs = torch.zeros(nq, 32, 128, dtype=torch.bfloat16)
+    assert D.indexer_topk_workspace(qs, w[:, :32], ki, cu_q, used, cu_kv, 100000, topk=2048) == nq * 100032 * 4

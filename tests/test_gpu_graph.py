@@ -11,7 +11,9 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("name,kw", [("inseq_cp8_last_8k", {"lens": (4096,)}),
-                                     ("rr_cp4_r1_var8_cmp4", {"lens": (3000, 901, 2200)})])
+                                     ("rr_cp4_r1_var8_cmp4", {"lens": (3000, 901, 2200)}),
+                                     # rows past 98304 keys: the candidate-list kernels in the graph
+                                     ("inseq_cp8_last_8k", {"lens": (100000,)})])
 def test_graph_replays_equal_eager(name, kw):
     dev = gpu()
     import sparse_attention_prefill_amd as D

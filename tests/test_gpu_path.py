@@ -125,9 +125,11 @@ def test_path_integer_inputs_topk_exact(name, kw):
     check_against_oracle(wl, "int", res, rows=rows)
 
 
-@pytest.mark.parametrize("name", ["long_131k_fp8", "chunk_inseq_cp8_last_8k_p56k"])
+@pytest.mark.parametrize("name", ["inseq_cp8_last_8k", "rr_cp8_r3_batch4", "long_131k_fp8", "rr_cp4_r1_var8_cmp4",
+                                  "chunk_inseq_cp8_last_8k_p56k", "rr_cp4_r1_var8_cmp128"])
 def test_path_full_size_integer_inputs_sampled(name):
-    """Rows longer than 32768 keys take the candidate-list top-k; integer inputs make it exact."""
+    """Full-size workloads with integer-valued indexer inputs: every score is exact on both sides,
+    so the top-k rows must be identical (the 131072-token rank selects from candidate lists)."""
     dev = gpu()
     wl = S.WORKLOADS[name]
     res = gpu_rank_path(wl, "int", dev)
