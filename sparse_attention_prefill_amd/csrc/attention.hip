@@ -414,7 +414,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
         float tmax = -INFINITY;
 #pragma unroll
         for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, s[v]);
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * scale_log2;
+        tmax = xor32_max(tmax) * scale_log2;
         m_seen = fmaxf(m_seen, tmax);
         if (attempt == 0 && t == 0 && hb == 0) {
           // O is still zero: fix the reference max here, no rescale needed
@@ -435,7 +435,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
             pa[kk][jj] = (__bf16)p;
           }
         }
-        psum += __shfl_xor(psum, 32, 64);
+        psum = xor32_sum(psum);
         l_run += psum;
 
         // O[h][d] += P[h][n] V[n][d]; k-slot jj of step kk is row 32hb + 16kk + 8(jj/4) + 4half + jj%4

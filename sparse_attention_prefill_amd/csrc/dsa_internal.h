@@ -136,6 +136,18 @@ __device__ inline float key_to_float(uint32_t k) {
   return k >= 0x80000000u ? __uint_as_float(k - 0x80000000u) : __uint_as_float((0x80000000u - k) | 0x80000000u);
 }
 
+// x[l] + x[l ^ 32] (and the max) in every lane of a wave: one VALU lane swap between the two
+// 32-lane halves instead of an LDS permute round trip. The two swap outputs hold x[l] and
+// x[l ^ 32] in every lane, so the sum is the same float as x[l] + x[l ^ 32] by commutativity.
+__device__ inline float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ inline float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 __device__ inline uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
 // lanes below this one whose bit is set in m
 __device__ inline int lanes_below(uint64_t m) {

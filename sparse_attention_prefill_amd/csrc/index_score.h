@@ -40,38 +40,8 @@ __device__ inline float head_weight(const float* __restrict__ w, const float* __
   return wt;
 }
 
-// The weights of one wave in LDS: wl[half][16m + r] = head_weight(m, r, half). The 32 lanes of a
-// half read the same addresses, so the epilogue reads them as broadcasts, four at a time, instead
-// of keeping 32 of them in VGPRs.
-template <bool FP8>
-__device__ inline void store_head_weights(const float* __restrict__ w, const float* __restrict__ q_scale, int i,
-                                          float (*wl)[32]) {
-  const int lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
-  wl[half][l32] = head_weight<FP8>(w, q_scale, i, l32 >> 4, l32 & 15, half);
-}
-
 // Query operands of row i for this lane: qa[m][ks] (heads 32m + (lane & 31)) and the weights of
 // the 16 heads the lane holds per chain, in output layout (times q_scale for fp8).
-template <bool FP8>
-__device__ inline void load_query_a(const unsigned char* __restrict__ qi, int i,
-                                    typename IdxOps<FP8>::AOp (&qa)[2][IdxOps<FP8>::kKsteps]) {
-  const int lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
-#pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    const unsigned char* qrow = qi + (int64_t(i) * kIdxHeads + 32 * m + l32) * IdxOps<FP8>::kKeyBytes;
-#pragma unroll
-    for (int ks = 0; ks < IdxOps<FP8>::kKsteps; ++ks) {
-      if constexpr (FP8) {
-        const i32x4* p = reinterpret_cast<const i32x4*>(qrow + 64 * ks + 32 * half);
-        const i32x4 x0 = p[0], x1 = p[1];
-        qa[m][ks] = i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-      } else {
-        qa[m][ks] = *reinterpret_cast<const bf16x8*>(qrow + 2 * (16 * ks + 8 * half));
-      }
-    }
-  }
-}
-
 template <bool FP8>
 __device__ inline void load_query_operands(const unsigned char* __restrict__ qi, const float* __restrict__ w,
                                            const float* __restrict__ q_scale, int i,
@@ -125,24 +95,7 @@ __device__ inline float block_head_sum(const float (&wv)[2][16], const f32x16& a
     sacc = fmaf(wv[0][r], relu_bits(a0[r]), sacc);
     sacc = fmaf(wv[1][r], relu_bits(a1[r]), sacc);
   }
-  return sacc + __shfl_xor(sacc, 32, 64);
-}
-
-// block_head_sum with the weights read from LDS (wl: this half's 32 weights, see
-// store_head_weights); the same operations in the same order
-__device__ inline float block_head_sum_lds(const float* wl, const f32x16& a0, const f32x16& a1) {
-  float sacc = 0.f;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const f32x4 w0 = *reinterpret_cast<const f32x4*>(wl + 4 * q);
-    const f32x4 w1 = *reinterpret_cast<const f32x4*>(wl + 16 + 4 * q);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      sacc = fmaf(w0[k], relu_bits(a0[4 * q + k]), sacc);
-      sacc = fmaf(w1[k], relu_bits(a1[4 * q + k]), sacc);
-    }
-  }
-  return sacc + __shfl_xor(sacc, 32, 64);
+  return xor32_sum(sacc);
 }
 
 // B operand of k-step ks read straight from key row `row` in global memory
