@@ -11,7 +11,7 @@
 // Two kernels:
 //  * sparse_attn_mla_bf16: 128 heads x 576 (value = first 512 columns), bf16 in, fp32 accumulate.
 //    One workgroup per query, 4 waves x 32 heads. The selected rows are gathered once per query
-//    into LDS, 64 rows (72 KiB) per tile, double-buffered with direct global->LDS loads that are
+//    into LDS, 64 rows (73 KiB) per tile, double-buffered with direct global->LDS loads that are
 //    issued between the first half-tile's logit MFMAs (one load per two MFMAs); every
 //    wave then runs S^T = K Q^T (32 rows x 32 heads, Q^T held in VGPRs) and O += P V on
 //    32x32x16 bf16 MFMAs. S^T puts one head per lane, so the softmax reductions are in-lane,
@@ -148,10 +148,11 @@ constexpr int kH = 128, kDqk = 576, kDv = 512;
 constexpr int kWaves = 4, kThreads = kWaves * 64;
 constexpr int kTile = 64;                          // KV rows per LDS tile
 constexpr int kRowBytes = kDqk * 2;                // 1152 bytes per KV row in HBM
-constexpr int kLatBytes = kDv * 2;                 // 1024: latent columns of a row in LDS
+constexpr int kLatBytes = kDv * 2;                 // 1024: latent columns of a row
+constexpr int kLatPitch = kLatBytes + 16;          // 1040: latent row pitch in LDS (16-byte skew per row)
 constexpr int kRopeBytes = kRowBytes - kLatBytes;  // 128: rope columns
-constexpr int kLatTile = kTile * kLatBytes;        // 64 KiB
-constexpr int kTileBytes = kLatTile + kTile * kRopeBytes;  // 72 KiB
+constexpr int kLatTile = kTile * kLatPitch;        // 65 KiB
+constexpr int kTileBytes = kLatTile + kTile * kRopeBytes;  // 73 KiB
 constexpr int kMaxKtot = 2304;                     // selected rows per query held in LDS (9 KiB)
 constexpr int kLoadsPerWave = 18;                  // 16 latent rows + 2 rope instructions
 static_assert(kDqk / 32 == kLoadsPerWave, "one gather load per two logit MFMAs of a half-tile");
@@ -164,16 +165,21 @@ static_assert(kDqk / 32 == kLoadsPerWave, "one gather load per two logit MFMAs o
 constexpr int kLookK = DSA_LOOKK, kLookV = DSA_LOOKV;  // LDS operand reads issued ahead of their MFMA
 constexpr float kOverflowMargin = 64.f;            // log2 units: e^(l - m) stays <= 2^64
 
-// LDS tile layout: latent region [64 rows][64 chunks of 16 B], then rope region [64 rows][8
-// chunks]. Chunk c of latent row n sits at physical chunk c ^ lat_swz(n), of rope row n at
-// c ^ rope_swz(n). lat_swz permutes the 16-chunk groups so that (a) the 16 rows of one K operand
-// read (same logical chunk) hit 16 distinct 16-byte bank groups and (b) each transposed V read
-// (4 consecutive rows x 32 contiguous bytes per 16-lane group, 4 rows x 64 bytes per 32 lanes)
-// touches distinct banks; both hold for 32 or 64 four-byte banks. rope_swz does (a) for 128-byte
-// rows.
-__device__ inline int lat_swz(int n) {
-  const int j = n & 3, b = (n >> 2) & 1, a = (n >> 3) & 1;
-  return ((((j >> 1) ^ a) << 3) | ((j & 1) << 2) | ((j >> 1) << 1) | b);
+// LDS tile layout: latent region [64 rows][1040 bytes] (the 1024 latent bytes of a row, then 16
+// unused), then rope region [64 rows][8 chunks of 16 B] with chunk c of row n at physical chunk
+// c ^ rope_swz(n). The 16-byte skew of the latent rows puts row n on banks shifted by 16n bytes,
+// so (a) the 16 rows of one K operand read (same column) hit 16 distinct 16-byte bank groups, and
+// (b) a transposed V read, whose 4 rows per 16 lanes are 4 rows apart (see row_of_mfma_row),
+// covers 256 contiguous bytes modulo the bank width. No address XOR is needed, so every latent
+// operand read is a per-lane base plus an immediate offset. rope_swz does (a) for 128-byte rows.
+//
+// MFMA row m of a 32-row half-tile reads tile row row_of_mfma_row(m): writing m = 8a + 4b + c
+// (a < 4, b < 2, c < 4), the row is 16(a/2) + 4c + 2(a%2) + b. The S^T accumulator gives lane
+// (half b) rows m = 8(v/4) + 4b + v%4, so the four rows v%4 = 0..3 that one transposed V read
+// gathers per 16 lanes are 4 tile rows apart.
+__device__ inline int row_of_mfma_row(int m) {
+  const int a = m >> 3, b = (m >> 2) & 1, c = m & 3;
+  return 16 * (a >> 1) + 4 * c + 2 * (a & 1) + b;
 }
 __device__ inline int rope_swz(int n) { return ((n >> 1) & 3) | (((n ^ (n >> 3)) & 1) << 2); }
 
@@ -264,7 +270,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
 
   // ---- gather of one tile into LDS with direct global->LDS loads ----
   //  latent: instruction j of this wave moves row n = 16*wave + j (one uniform row id, 64 lanes x
-  //          16 B = 1024 B; lane l lands in physical chunk l, i.e. logical chunk l ^ lat_swz(n));
+  //          16 B = 1024 B; lane l lands in chunk l of the row);
   //  rope:   2 instructions of 8 rows x 8 chunks (lane l: row 8r + l/8, physical chunk l%8).
   const unsigned char* kvb = reinterpret_cast<const unsigned char*>(kv);
   // The row ids a wave needs for tile t: lane l holds latent row 16*wave + (l & 15) and, for
@@ -283,8 +289,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
     const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_offset(tiles + buf * kTileBytes));
     if (j < 16) {
       const int r = __builtin_amdgcn_readlane(gr.lat, j);
-      lds_dma16_s(kvb + int64_t(r) * kRowBytes, uint32_t(lane16 ^ (lat_swz(j) << 4)),  // (16w+j)&15 == j
-                  dst + uint32_t((16 * wave + j) * kLatBytes));
+      lds_dma16_s(kvb + int64_t(r) * kRowBytes, uint32_t(lane16), dst + uint32_t((16 * wave + j) * kLatPitch));
     } else {
       const int n0 = 16 * wave + 8 * (j - 16);  // rows n0 + lane/8
       const int c = (lane & 7) ^ rope_swz(n0 + (lane >> 3));
@@ -298,27 +303,17 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
     for (int j = 0; j < kLoadsPerWave; ++j) gather_one(gr, buf, j);
   };
 
-  // per-lane LDS byte offsets (tile-relative). A swizzled chunk offset is (c << 4) ^ (f << 4); the
-  // XOR with the per-lane part is done per read (one VALU op) instead of holding every variant:
-  //  K operand (rows n = 32hb + l32, logical chunk 2ks + half):
-  //      k_base + ((32 ks) ^ k_x) + 32hb*1024      [k_x = (half ^ lat_swz(l32)) << 4]
-  //  rope operand (logical chunk 2(ks-32) + half): r_base + ((32 (ks-32)) ^ r_x) + 32hb*128
-  //  transposed V reads (see lds_read_tr16): lane L supplies row v_n = 4*(L/32) + (L%16)/4 of an
-  //  8-row slab (lo: rows 16kk + v_n, hi: 16kk + 8 + v_n) and columns 32db + 16((L/16)&1) +
-  //  4(L%4) .. +3 (logical chunk 4db + v_cl): v_base[hl] + ((64 db) ^ v_x[hl])
-  const int k_base = l32 * kLatBytes, k_x0 = (half ^ lat_swz(l32)) << 4;
-  const int r_base = kLatTile + l32 * kRopeBytes, r_x0 = (half ^ rope_swz(l32)) << 4;
-  int v_base[2], v_x0[2];
-  {
-    const int v_n = 4 * half + ((lane & 15) >> 2);
-    const int v_cl = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-#pragma unroll
-    for (int hl = 0; hl < 2; ++hl) {
-      const int n = v_n + 8 * hl;
-      v_base[hl] = n * kLatBytes + ((lane & 1) << 3);
-      v_x0[hl] = (v_cl ^ lat_swz(n)) << 4;
-    }
-  }
+  // per-lane LDS byte offsets (tile-relative); the rest of each address is an immediate offset:
+  //  K operand of half-tile hb, k-step ks < 32 (tile row 32hb + row_of_mfma_row(l32), latent
+  //      chunk 2ks + half): k_base + 32hb*1040 + 32ks
+  //  rope operand (chunk 2(ks-32) + half): r_base + 32hb*128 + ((32 (ks-32)) ^ r_x)
+  //  transposed V reads (see lds_read_tr16) of P.V step kk: lane L supplies tile row
+  //      32hb + 16kk + 2hl + 4((L%16)/4) + L/32 (hl = 0: k-slots 0..3 of its half, hl = 1: 4..7)
+  //      and columns 32db + 16((L/16)&1) + 4(L%4) .. +3: v_base + (32hb + 16kk + 2hl)*1040 + 64db
+  const int k_row = row_of_mfma_row(l32);
+  const int k_base = k_row * kLatPitch + 16 * half;
+  const int r_base = kLatTile + k_row * kRopeBytes, r_x0 = (half ^ rope_swz(k_row)) << 4;
+  const int v_base = (4 * ((lane & 15) >> 2) + half) * kLatPitch + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
 
   const float sink_l2 = sink ? sink[h] * kLog2e : -INFINITY;
   f32x16 oacc[kDv / 32];
@@ -361,10 +356,10 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
         if (hb == 0 && gather_next) {
           // explicit software pipeline: kLookK operand reads ahead; after every second MFMA one
           // gather load (its memory clobber keeps the operand reads in this order)
-          int k_x = k_x0, r_x = r_x0;
-          asm volatile("" : "+v"(k_x), "+v"(r_x));
+          int r_x = r_x0;
+          asm volatile("" : "+v"(r_x));
           auto k_read = [&](int ks) {
-            return ks < kDv / 16 ? *reinterpret_cast<const bf16x8*>(tb + k_base + ((32 * ks) ^ k_x))
+            return ks < kDv / 16 ? *reinterpret_cast<const bf16x8*>(tb + k_base + 32 * ks)
                                  : *reinterpret_cast<const bf16x8*>(tb + r_base + ((32 * (ks - kDv / 16)) ^ r_x));
           };
           bf16x8 a[kDqk / 16];
@@ -381,12 +376,12 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
             gather_one(gr, buf ^ 1, c);
           }
         } else {
-          int k_x = k_x0, r_x = r_x0;
-          asm volatile("" : "+v"(k_x), "+v"(r_x));  // recomputed per half-tile: no hoisting of 36 offsets
+          int r_x = r_x0;
+          asm volatile("" : "+v"(r_x));  // recomputed per half-tile: no hoisting of the rope offsets
           bf16x8 a[kDqk / 16];
 #pragma unroll
           for (int ks = 0; ks < kDv / 16; ++ks)
-            a[ks] = *reinterpret_cast<const bf16x8*>(tb + k_base + ((32 * ks) ^ k_x) + 32 * hb * kLatBytes);
+            a[ks] = *reinterpret_cast<const bf16x8*>(tb + k_base + 32 * hb * kLatPitch + 32 * ks);
 #pragma unroll
           for (int ks = kDv / 16; ks < kDqk / 16; ++ks)
             a[ks] = *reinterpret_cast<const bf16x8*>(tb + r_base + ((32 * (ks - kDv / 16)) ^ r_x) + 32 * hb * kRopeBytes);
@@ -402,14 +397,15 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
           __builtin_amdgcn_sched_group_barrier(0x008, kLookK, 0);
         }
 
-        // lane holds rows n = 32hb + 8(v/4) + 4half + v%4 of head h; mask rows past the selection
-        // (only the last tile can be partial: wave-uniform branch)
+        // register v of the lane holds tile row 32hb + row_of_mfma_row(8(v/4) + 4half + v%4) =
+        // 32hb + 16(v/8) + 4(v%4) + 2((v/4)%2) + half of head h; mask rows past the selection (only
+        // the last tile can be partial: wave-uniform branch)
         // (raw logits; the positive scale is applied inside the exponent below)
         if (valid < kTile) {
-          const int lim = valid - 32 * hb - 4 * half;
+          const int lim = valid - 32 * hb - half;
 #pragma unroll
           for (int v = 0; v < 16; ++v)
-            if (8 * (v >> 2) + (v & 3) >= lim) s[v] = -INFINITY;
+            if (16 * (v >> 3) + 4 * (v & 3) + 2 * ((v >> 2) & 1) >= lim) s[v] = -INFINITY;
         }
         float tmax = -INFINITY;
 #pragma unroll
@@ -438,17 +434,16 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
         psum = xor32_sum(psum);
         l_run += psum;
 
-        // O[h][d] += P[h][n] V[n][d]; k-slot jj of step kk is row 32hb + 16kk + 8(jj/4) + 4half + jj%4
+        // O[h][d] += P[h][n] V[n][d]; k-slot 8half + jj of step kk is the S^T row of register
+        // 8kk + jj: tile row 32hb + 16kk + 4(jj%4) + 2(jj/4) + half
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-          const unsigned char* vb = tb + (32 * hb + 16 * kk) * kLatBytes;
-          int vx0 = v_x0[0], vx1 = v_x0[1];
-          asm volatile("" : "+v"(vx0), "+v"(vx1));
+          const unsigned char* vb = tb + v_base + (32 * hb + 16 * kk) * kLatPitch;
           s16x4 lo[kDv / 32], hi[kDv / 32];
 #pragma unroll
           for (int db = 0; db < kDv / 32; ++db) {
-            lo[db] = lds_read_tr16(vb + v_base[0] + ((64 * db) ^ vx0));
-            hi[db] = lds_read_tr16(vb + v_base[1] + ((64 * db) ^ vx1));
+            lo[db] = lds_read_tr16(vb + 64 * db);
+            hi[db] = lds_read_tr16(vb + 2 * kLatPitch + 64 * db);
           }
 #pragma unroll
           for (int db = 0; db < kDv / 32; ++db) {
