@@ -236,3 +236,77 @@ def test_attention_flags_bad_rows():
                   to_dev(inp["sink"], "f32", dev), 0.05, 512, err_flag=err)
     torch.cuda.synchronize()
     assert err.item() & 0x40
+
+
+def test_attention_reruns_when_a_late_logit_is_far_above_the_first_rows():
+    """The kernel takes each head's reference max from the first 32 selected rows (and the sink);
+    a later row whose logit exceeds it by more than 64 (log2 units) makes the workgroup rerun the
+    query with the exact max. Query 0 meets such a row at selection position 150 (third 64-row
+    tile), 173 log2 units above the first rows: without the rerun its probabilities would overflow
+    fp32. Query 1 meets an equally large logit at position 5, inside the first rows (no rerun);
+    query 2 has neither. All three must match the oracle."""
+    dev = gpu()
+    import sparse_attention_prefill_amd as D
+    n_rows, k_tot, nq = 512, 256, 3
+    wl = S.WORKLOADS["inseq_cp8_last_8k"].with_(lens=(n_rows,))
+    inp = S.stream_inputs(wl, "unit")
+    qin = S.query_inputs(wl, np.arange(nq) * 5, "unit")
+    scale = 1.0 / np.sqrt(wl.Dqk)
+    q = O.decode(qin["q"], "bf16")
+    kv_bits = inp["kv"].copy()
+    big = {0: (7, 3, 150), 1: (11, 5, 5)}  # query: (kv row, head it aligns with, selection position)
+    for i, (row, head, _) in big.items():
+        # rope columns along q[i, head]'s: they add 120 nats to the logit of (i, head) on this row
+        # and, not being value columns, leave the outputs O(1)
+        r = q[i, head, wl.Dv:]
+        kv_row = O.decode(kv_bits[row], "bf16").copy()
+        kv_row[wl.Dv:] = 120.0 / (scale * np.linalg.norm(r)) * r / np.linalg.norm(r)
+        kv_bits[row] = S.f64_to_bf16_bits(kv_row)
+    g = np.random.default_rng(5)
+    others = np.setdiff1d(np.arange(n_rows), [row for row, _, _ in big.values()])
+    idx = np.stack([g.permutation(others)[:k_tot] for _ in range(nq)]).astype(np.int32)
+    for i, (row, _, pos) in big.items():
+        idx[i, pos] = row
+    kv = O.decode(kv_bits, "bf16")
+    sink = inp["sink"].astype(np.float64)
+    first = [float((q[i] @ kv[idx[i, :32]].T).max() * scale) for i in range(nq)]
+    late = [float((q[i] @ kv[idx[i, 32:]].T).max() * scale) for i in range(nq)]
+    assert (late[0] - max(first[0], sink.max())) / np.log(2) > 128  # query 0 overflows without the rerun
+    assert (late[1] - max(first[1], sink.max())) / np.log(2) < 64  # query 1 does not
+    lse = torch.empty(nq, wl.H, dtype=torch.float32, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    out = D.sparse_attn(to_dev(qin["q"], "bf16", dev), to_dev(kv_bits, "bf16", dev), to_dev(idx, "i32", dev),
+                        to_dev(inp["sink"], "f32", dev), scale, wl.Dv, lse=lse, err_flag=err)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    ref = np.zeros((nq, wl.H, wl.Dv))
+    ref_lse = np.zeros((nq, wl.H))
+    for i in range(nq):
+        ref[i], ref_lse[i] = O.sparse_attention_row(q[i], kv[idx[i]], sink, scale, wl.Dv)
+    assert_attn_close(to_f64(out), ref, "bf16", "late large logit")
+    assert np.abs(lse.cpu().numpy() - ref_lse).max() < 2e-3
+
+
+def test_attention_largest_selection_and_one_past_it():
+    """k_tot = 2304 (the most selected rows per query the MLA kernel holds) matches the oracle;
+    2305 is refused before any launch."""
+    dev = gpu()
+    import sparse_attention_prefill_amd as D
+    n_rows, nq = 4096, 3
+    wl = S.WORKLOADS["inseq_cp8_last_8k"].with_(lens=(n_rows,))
+    inp = S.stream_inputs(wl)
+    qin = S.query_inputs(wl, np.arange(nq) * 11)
+    scale = 1.0 / np.sqrt(wl.Dqk)
+    g = np.random.default_rng(9)
+    idx = np.stack([g.permutation(n_rows)[:2304] for _ in range(nq)]).astype(np.int32)
+    idx[2, 2300:] = -1  # a ragged last tile
+    q_d, kv_d, s_d = to_dev(qin["q"], "bf16", dev), to_dev(inp["kv"], "bf16", dev), to_dev(inp["sink"], "f32", dev)
+    out = D.sparse_attn(q_d, kv_d, to_dev(idx, "i32", dev), s_d, scale, wl.Dv)
+    torch.cuda.synchronize()
+    kv = O.decode(inp["kv"], "bf16")
+    sink = inp["sink"].astype(np.float64)
+    ref = np.stack([O.sparse_attention_row(O.decode(qin["q"][i], "bf16"), kv[idx[i][idx[i] >= 0]], sink, scale,
+                                           wl.Dv)[0] for i in range(nq)])
+    assert_attn_close(to_f64(out), ref, "bf16", "k_tot 2304")
+    with pytest.raises(D.DsaError, match="2304"):
+        D.sparse_attn(q_d, kv_d, to_dev(np.zeros((nq, 2305), np.int32), "i32", dev), s_d, scale, wl.Dv)
