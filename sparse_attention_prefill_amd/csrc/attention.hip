@@ -17,9 +17,10 @@
 //    32x32x16 bf16 MFMAs. S^T puts one head per lane, so the softmax reductions are in-lane,
 //    and its accumulator layout is directly the A operand of P V (the contraction order over
 //    rows is permuted identically on both operands). The softmax reference max m of each head is
-//    fixed from the first tile (and the sink), so O is never rescaled: every later probability is
-//    e^(l - m) <= 2^64, far inside fp32 / bf16 range. If a later logit ever exceeds m by more
-//    than that, the workgroup reruns the query once with m = the exact max seen in the first run.
+//    fixed from the first 32 selected rows (and the sink), so O is never rescaled. A pass is kept
+//    when every head's denominator stays <= 2^64 (which bounds every probability by 2^64, far
+//    inside fp32 / bf16 range); otherwise the workgroup sweeps the query's logits for their exact
+//    max and reruns it with that max.
 //  * sparse_attn_generic: float32 or bf16, small head counts (n_heads * d_v <= 4096); VALU.
 #include "dsa_internal.h"
 
@@ -163,7 +164,7 @@ static_assert(kDqk / 32 == kLoadsPerWave, "one gather load per two logit MFMAs o
 #define DSA_LOOKV 2
 #endif
 constexpr int kLookK = DSA_LOOKK, kLookV = DSA_LOOKV;  // LDS operand reads issued ahead of their MFMA
-constexpr float kOverflowMargin = 64.f;            // log2 units: e^(l - m) stays <= 2^64
+constexpr float kMaxDenominator = 0x1p64f;         // a pass is kept while every head's sum of e^(l - m) <= 2^64
 
 // LDS tile layout: latent region [64 rows][1040 bytes] (the 1024 latent bytes of a row, then 16
 // unused), then rope region [64 rows][8 chunks of 16 B] with chunk c of row n at physical chunk
@@ -325,15 +326,50 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
   // gather loads. Encoding: vmcnt(0), expcnt and lgkmcnt left at their maximum.
   __builtin_amdgcn_s_waitcnt(0x0F70);
 
+  // Logits-only sweep over the selection (the rare rerun): the exact max of this lane's head's
+  // logits, in log2 units. Same gather and logit MFMAs as the main pass, without the pipelining.
+  auto max_sweep = [&]() {
+    float mx = -INFINITY;
+    if (n_tiles > 0) issue_tile(0, 0);
+#pragma unroll 1
+    for (int t = 0; t < n_tiles; ++t) {
+      DSA_TILE_BARRIER_VMCNT(0);  // tile t landed; every wave is done with tile t - 1's buffer
+      if (t + 1 < n_tiles) issue_tile(t + 1, (t + 1) & 1);
+      const unsigned char* tb = tiles + (t & 1) * kTileBytes;
+      const int valid = n_sel - t * kTile;
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        f32x16 s = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < kDqk / 16; ++ks) {
+          const bf16x8 a = ks < kDv / 16
+                               ? *reinterpret_cast<const bf16x8*>(tb + k_base + 32 * hb * kLatPitch + 32 * ks)
+                               : *reinterpret_cast<const bf16x8*>(tb + r_base + 32 * hb * kRopeBytes +
+                                                                  ((32 * (ks - kDv / 16)) ^ r_x0));
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], s, 0, 0, 0);
+        }
+        const int lim = valid - 32 * hb - half;
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          if (16 * (v >> 3) + 4 * (v & 3) + 2 * ((v >> 2) & 1) < lim) tmax = fmaxf(tmax, s[v]);
+        mx = fmaxf(mx, xor32_max(tmax) * scale_log2);
+      }
+    }
+    DSA_TILE_BARRIER_LDS();  // every wave is done reading before the next pass refills the buffers
+    return mx;
+  };
+
 #pragma unroll 1
   for (int attempt = 0; attempt < 2; ++attempt) {
-    // attempt 0: m from the first tile; attempt 1 (rare): m = exact max of every logit seen
+    // attempt 0: m from the first 32 selected rows (and the sink); attempt 1 runs only when a
+    // head's denominator overflowed the bound, with m = the exact max from a logits-only sweep
     // (an empty selection keeps m = sink, l = 1: out = 0, lse = sink)
+    if (attempt == 1) m_seen = max_sweep();
     m_used = attempt == 0 ? sink_l2 : fmaxf(sink_l2, m_seen);
     l_run = sink ? exp2f(sink_l2 - m_used) : 0.f;
 #pragma unroll
     for (int db = 0; db < kDv / 32; ++db) oacc[db] = f32x16{};
-    bool overflow = false;
 
     if (n_tiles > 0) issue_tile(0, 0);
     for (int t = 0; t < n_tiles; ++t) {
@@ -401,23 +437,20 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
         // 32hb + 16(v/8) + 4(v%4) + 2((v/4)%2) + half of head h; mask rows past the selection (only
         // the last tile can be partial: wave-uniform branch)
         // (raw logits; the positive scale is applied inside the exponent below)
-        if (valid < kTile) {
+        if (__builtin_expect(valid < kTile, 0)) {  // kept a branch: selects on every tile cost VALU
           const int lim = valid - 32 * hb - half;
 #pragma unroll
           for (int v = 0; v < 16; ++v)
             if (16 * (v >> 3) + 4 * (v & 3) + 2 * ((v >> 2) & 1) >= lim) s[v] = -INFINITY;
         }
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, s[v]);
-        tmax = xor32_max(tmax) * scale_log2;
-        m_seen = fmaxf(m_seen, tmax);
-        if (attempt == 0 && t == 0 && hb == 0) {
+        if (attempt == 0 && t == 0 && hb == 0) {  // uniform
           // O is still zero: fix the reference max here, no rescale needed
-          m_used = fmaxf(sink_l2, tmax);
+          float tmax = -INFINITY;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, s[v]);
+          m_used = fmaxf(sink_l2, xor32_max(tmax) * scale_log2);
           l_run = sink ? exp2f(sink_l2 - m_used) : 0.f;
         }
-        overflow |= tmax > m_used + kOverflowMargin;
 
         // probabilities (bf16) in the P.V A-operand layout; row sums
         float psum = 0.f;
@@ -462,6 +495,9 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
       }
     }
     if (attempt == 0) {
+      // every probability is at most its head's denominator, so l_run <= 2^64 bounds them all
+      // (and the O sums) far inside the fp32 / bf16 range; inf or NaN also fail the test
+      const bool overflow = !(l_run <= kMaxDenominator);
       if (__any(overflow) && lane == 0) atomicOr(redo_flag, 1);
       __syncthreads();
       if (*redo_flag == 0) break;  // uniform
