@@ -39,6 +39,7 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 // and for its LDS reads; the memory clobber keeps the compiler from moving accesses across.
 #define DSA_TILE_BARRIER_VMCNT(n) asm volatile("s_waitcnt vmcnt(" #n ")\n\ts_barrier" ::: "memory")
 #define DSA_TILE_BARRIER_LDS() asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
+#define DSA_TILE_BARRIER_ALL() asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory")
 
 // Direct global->LDS 16-byte loads: lane l's 16 bytes land at lds_base + 16*l (lds_base is
 // wave-uniform, passed in M0). Issued as inline asm so the compiler does not add its own

@@ -87,7 +87,6 @@ struct IdxCfg {
   static constexpr int kChunks = kKeyBytes / 16;                  // 8 or 16
   static constexpr int kTileBytes = kKeyTile * kKeyBytes;         // 32 or 64 KiB
   static constexpr int kLoads = kKeyTile * kChunks / kThreads;    // direct loads per lane per tile: 4 or 8
-  static constexpr int kInFlight = kLoads + (FP8 ? 1 : 0);        // the next tile's loads (fp8: + its scales)
 };
 
 // bf16: one workgroup per CU (its 64 x 128 query operand takes 64 VGPRs per lane), with the
@@ -200,17 +199,12 @@ __global__ __launch_bounds__(kThreads, FP8 ? 4 : 1) void indexer_mfma(
     issue_tile(0, 0);
     for (int t = 0; t < n_tiles; ++t) {
       const int buf = t & 1;
+      // One barrier per tile: after it, tile t has landed for every wave and every wave is done
+      // with tile t - 1, whose buffer then takes tile t + 1 (loaded while tile t is computed).
+      DSA_TILE_BARRIER_ALL();
       if (t + 1 < n_tiles) {
         issue_kscale(t + 1, buf ^ 1);
         issue_tile(t + 1, buf ^ 1);
-        // the next tile's loads (and its scales for fp8) may stay in flight
-        if constexpr (C::kInFlight == 3) DSA_TILE_BARRIER_VMCNT(3);
-        else if constexpr (C::kInFlight == 4) DSA_TILE_BARRIER_VMCNT(4);
-        else if constexpr (C::kInFlight == 5) DSA_TILE_BARRIER_VMCNT(5);
-        else if constexpr (C::kInFlight == 8) DSA_TILE_BARRIER_VMCNT(8);
-        else static_assert(C::kInFlight == 3, "no barrier for this tile size");
-      } else {
-        DSA_TILE_BARRIER_VMCNT(0);
       }
       const int key0 = glo + t * kKeyTile;
       if (ok && key0 < hi_c && key0 + kKeyTile > lo_c) {  // wave-uniform
@@ -258,8 +252,8 @@ __global__ __launch_bounds__(kThreads, FP8 ? 4 : 1) void indexer_mfma(
           }
         }
       }
-      DSA_TILE_BARRIER_LDS();
     }
+    DSA_TILE_BARRIER_LDS();  // every wave is done with this chunk's buffers before the next chunk's first tile
   }
   if (CAND && cand_row && lane == 0) n_cand[int64_t(i) * gridDim.y + blockIdx.y] = st_n;
 }
