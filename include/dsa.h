@@ -191,8 +191,11 @@ dsa_status dsa_topk_from_scores(const dsa_indexer_topk_args* args, const float* 
  *   out[i,h,:] = sum_s e^(l_s) kv[s, 0:d_v] / (e^(sink[h]) + sum_s e^(l_s))
  *   lse[i,h]   = ln(e^(sink[h]) + sum_s e^(l_s))
  * (no sink: sink == NULL drops the e^(sink) term). Accumulation is float32; out has q's dtype.
- * Supported: (n_heads, d_qk, d_v, dtype) = (128, 576, 512, bf16), and float32 with
- * n_heads * d_v <= 4096, d_qk <= 512.
+ * Supported: (n_heads, d_qk, d_v, dtype) = (128, 576, 512, bf16) with k_tot <= 2304 (matrix
+ * cores), and float32 or bf16 with n_heads * d_v <= 4096, d_qk <= 512 and
+ * n_heads * d_qk <= 16384 (vector ALU); anything else returns DSA_ERR_UNSUPPORTED. Row ids
+ * outside [-1, n_rows) set DSA_DEVERR_INDEX in *err_flag and are skipped. A query with no
+ * selected row gives out = 0 and lse = sink[h] (-inf without a sink).
  * ------------------------------------------------------------------------------------------ */
 typedef struct {
   const void* q;            /* device [nq, n_heads, d_qk]                                    */

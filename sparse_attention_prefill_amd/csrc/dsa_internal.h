@@ -32,11 +32,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-// Workgroup barrier for double-buffered direct global->LDS tile loads. __syncthreads() carries a
-// workgroup memory fence that waits for EVERY outstanding vector-memory load (vmcnt(0)),
-// including the next tile's prefetch, which would serialise load and compute. These barriers
-// wait only for this wave's loads of the current tile (the newest `n` loads may stay in flight)
-// and for its LDS reads; the memory clobber keeps the compiler from moving accesses across.
+// Workgroup barriers for double-buffered direct global->LDS tile loads, as inline asm so the
+// compiler adds no waits of its own (it cannot see the direct loads). VMCNT(n): this wave's
+// vector-memory operations except the newest n have completed (loads return in order, so a
+// prefetch issued just before may stay in flight); LDS: its LDS reads have returned; ALL: both.
+// The memory clobber keeps the compiler from moving accesses across.
 #define DSA_TILE_BARRIER_VMCNT(n) asm volatile("s_waitcnt vmcnt(" #n ")\n\ts_barrier" ::: "memory")
 #define DSA_TILE_BARRIER_LDS() asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
 #define DSA_TILE_BARRIER_ALL() asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory")

@@ -310,3 +310,35 @@ def test_attention_largest_selection_and_one_past_it():
     assert_attn_close(to_f64(out), ref, "bf16", "k_tot 2304")
     with pytest.raises(D.DsaError, match="2304"):
         D.sparse_attn(q_d, kv_d, to_dev(np.zeros((nq, 2305), np.int32), "i32", dev), s_d, scale, wl.Dv)
+
+
+@pytest.mark.parametrize("name", ["inseq_cp8_last_8k", "tiny_fp32_cp1"])
+def test_attention_without_sink(name):
+    """sink = NULL drops the e^(sink) term: the oracle with sink = -inf; a query whose selection is
+    empty gives out = 0 and lse = -inf."""
+    dev = gpu()
+    import sparse_attention_prefill_amd as D
+    n_rows, nq = 300, 5
+    wl = S.WORKLOADS[name].with_(lens=(n_rows,))
+    inp = S.stream_inputs(wl, "unit")
+    qin = S.query_inputs(wl, np.arange(nq) * 3, "unit")
+    kind = wl.attn_dtype
+    k_tot = 100 if kind == "bf16" else 64
+    idx = _rand_idx(np.random.default_rng(3), nq, k_tot, n_rows, empty_rows=(2,))
+    scale = 1.0 / np.sqrt(wl.Dqk)
+    lse = torch.empty(nq, wl.H, dtype=torch.float32, device=dev)
+    out = D.sparse_attn(to_dev(qin["q"], kind, dev), to_dev(inp["kv"], kind, dev), to_dev(idx, "i32", dev), None,
+                        scale, wl.Dv, lse=lse)
+    torch.cuda.synchronize()
+    kv = O.decode(inp["kv"], kind)
+    no_sink = np.full(wl.H, -np.inf)
+    ref = np.zeros((nq, wl.H, wl.Dv))
+    ref_lse = np.zeros((nq, wl.H))
+    for i in range(nq):
+        ref[i], ref_lse[i] = O.sparse_attention_row(O.decode(qin["q"][i], kind), kv[idx[i][idx[i] >= 0]], no_sink,
+                                                    scale, wl.Dv)
+    assert_attn_close(to_f64(out), ref, kind, f"{name} no sink")
+    got_lse = lse.cpu().numpy()
+    assert np.all(np.isneginf(got_lse[2])) and np.all(np.isneginf(ref_lse[2]))
+    live = np.arange(nq) != 2
+    assert np.abs(got_lse[live] - ref_lse[live]).max() < (1e-4 if kind == "f32" else 2e-3)
