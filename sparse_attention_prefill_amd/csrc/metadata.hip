@@ -11,8 +11,9 @@
 // n_b queries; its KV segment (seq_lens[b] rows, prefix first) follows the previous request's,
 // and every extent counts the prefix.
 //
-// One workgroup of 1024 threads computes every per-request value with closed forms (no loop
-// over tokens) and wavefront prefix scans; all workgroups fill the token map.
+// Every per-request value comes from closed forms (no loop over tokens) and prefix scans: one
+// wave with wave scans for batches of up to 64 requests (no workgroup barrier on the critical
+// path), else one workgroup of 1024 threads with block scans; all workgroups fill the token map.
 #include "dsa_internal.h"
 
 namespace dsa {
@@ -54,6 +55,41 @@ __device__ inline int block_excl_scan(int v, int* smem_waves, int* total) {
 // number of tokens t < x with t % cp == r
 __device__ inline int rr_count_below(int x, int cp, int r) { return x > r ? (x - r + cp - 1) / cp : 0; }
 
+// Request b: its local queries nb, its local KV extent ext (cached prefix included) and its KV
+// segment length seg; bad collects DSA_DEVERR_* bits of inconsistent input.
+struct RequestView {
+  int nb, ext, seg, bad;
+};
+__device__ inline RequestView request_view(const int32_t* __restrict__ qsl, const int32_t* __restrict__ seq_lens,
+                                           int b, int batch, int T, int cp, int rank, bool rr, int local_start,
+                                           int local_end) {
+  RequestView v{0, 0, 0, 0};
+  const int qs = qsl[b];
+  const int qe = qsl[b + 1];
+  if (b == 0 && qs != 0) v.bad |= DSA_DEVERR_QSL_START;
+  if (qe < qs) v.bad |= DSA_DEVERR_QSL_ORDER;
+  if (b == batch - 1 && qe != T) v.bad |= DSA_DEVERR_QSL_TOTAL;
+  const int len = max(qe - qs, 0);
+  int prefix = seq_lens[b] - len;
+  if (prefix < 0) {
+    v.bad |= DSA_DEVERR_SEQ_LENS;
+    prefix = 0;
+  }
+  v.seg = prefix + len;
+  if (rr) {
+    v.nb = max(rr_count_below(qe, cp, rank) - rr_count_below(qs, cp, rank), 0);
+    v.ext = prefix;
+    if (v.nb > 0) {
+      const int t_last = rank + (rr_count_below(qe, cp, rank) - 1) * cp;
+      v.ext += t_last - qs + 1;
+    }
+  } else {
+    v.nb = max(min(qe, local_end) - max(qs, local_start), 0);
+    v.ext = prefix + min(max(local_end - qs, 0), len);
+  }
+  return v;
+}
+
 __global__ __launch_bounds__(kThreads) void cp_metadata_kernel(
     const int32_t* __restrict__ qsl, const int32_t* __restrict__ seq_lens, int batch, int T, int cp,
     int rank, int mode, int32_t* __restrict__ lqsl, int32_t* __restrict__ lsl, int32_t* __restrict__ lkv,
@@ -79,6 +115,40 @@ __global__ __launch_bounds__(kThreads) void cp_metadata_kernel(
   }
   if (blockIdx.x != 0) return;
 
+  if (batch <= 64) {  // one wave (uniform branch)
+    if (threadIdx.x >= 64) return;
+    const int b = threadIdx.x;
+    RequestView v{0, 0, 0, 0};
+    if (b < batch) {
+      v = request_view(qsl, seq_lens, b, batch, T, cp, rank, rr, local_start, local_end);
+      lsl[b] = v.ext;
+      if (v.bad) raise_flag(err_flag, v.bad);
+    }
+    const int iq = wave_incl_scan(v.nb), ikv = wave_incl_scan(v.ext), iseg = wave_incl_scan(v.seg);
+    if (b < batch) {
+      lqsl[b] = iq - v.nb;
+      lkv[b] = rr ? iseg - v.seg : ikv - v.ext;
+    }
+    int mx = v.nb;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) mx = max(mx, __shfl_xor(mx, d, 64));
+    const int nreq = __popcll(__builtin_amdgcn_ballot_w64(v.nb > 0));
+    const int tot_q = __shfl(iq, 63, 64), tot_kv = __shfl(ikv, 63, 64), tot_seg = __shfl(iseg, 63, 64);
+    if (b == 0) {
+      lqsl[batch] = tot_q;
+      lkv[batch] = rr ? tot_seg : tot_kv;
+      scalars[0] = tpr * cp;
+      scalars[1] = tpr;
+      scalars[2] = local_start;
+      scalars[3] = local_end;
+      scalars[4] = rr ? cp : 1;
+      scalars[5] = rr ? rr_count_below(T, cp, rank) : local_end - local_start;
+      scalars[6] = mx;
+      scalars[7] = nreq;
+    }
+    return;
+  }
+
   __shared__ int smem[kWaves + 1];
   __shared__ int s_max, s_nreq;
   if (threadIdx.x == 0) {
@@ -93,29 +163,11 @@ __global__ __launch_bounds__(kThreads) void cp_metadata_kernel(
     const int b = base + threadIdx.x;
     int nb = 0, ext = 0, seg = 0;
     if (b < batch) {
-      const int qs = qsl[b];
-      const int qe = qsl[b + 1];
-      if (b == 0 && qs != 0) bad |= DSA_DEVERR_QSL_START;
-      if (qe < qs) bad |= DSA_DEVERR_QSL_ORDER;
-      if (b == batch - 1 && qe != T) bad |= DSA_DEVERR_QSL_TOTAL;
-      const int len = max(qe - qs, 0);
-      int prefix = seq_lens[b] - len;
-      if (prefix < 0) {
-        bad |= DSA_DEVERR_SEQ_LENS;
-        prefix = 0;
-      }
-      seg = prefix + len;
-      if (rr) {
-        nb = max(rr_count_below(qe, cp, rank) - rr_count_below(qs, cp, rank), 0);
-        ext = prefix;
-        if (nb > 0) {
-          const int t_last = rank + (rr_count_below(qe, cp, rank) - 1) * cp;
-          ext += t_last - qs + 1;
-        }
-      } else {
-        nb = max(min(qe, local_end) - max(qs, local_start), 0);
-        ext = prefix + min(max(local_end - qs, 0), len);
-      }
+      const RequestView v = request_view(qsl, seq_lens, b, batch, T, cp, rank, rr, local_start, local_end);
+      nb = v.nb;
+      ext = v.ext;
+      seg = v.seg;
+      bad |= v.bad;
       lsl[b] = ext;
       atomicMax(&s_max, nb);
       if (nb > 0) atomicAdd(&s_nreq, 1);

@@ -22,6 +22,8 @@ def _batches():
     for _ in range(12):
         B = int(g.integers(1, 40))
         yield [int(x) for x in g.integers(0, 300, size=B)]
+    for B in (64, 65, 300):  # the single-wave path's limit, just past it, several waves
+        yield [int(x) for x in g.integers(0, 50, size=B)]
     yield [int(x) for x in g.integers(0, 9, size=1100)]  # more requests than one workgroup pass
     yield []
 
