@@ -157,6 +157,10 @@ __global__ __launch_bounds__(kThreads, FP8 ? 4 : 1) void indexer_mfma(
   // register count; no atomics. The count is stored once at the end, overflow included.
   const bool cand_row = CAND && ok && hi - lo > fuse_above;  // wave-uniform
   const uint32_t theta_k = cand_row ? theta[i] : 0u;
+  // The same test on floats: theta_k is the 22-bit key prefix of a finite sample score, i.e. the
+  // key of a finite float (or of -inf), and keys grow with the float order (+0 and -0 share one),
+  // so for a finite score x, order_key(x) >= theta_k exactly when x >= theta_f.
+  const float theta_f = key_to_float(theta_k);
   const int seg_cap = cand_cap / int(gridDim.y);
   uint2* seg = CAND ? cand + int64_t(i) * cand_cap + int64_t(blockIdx.y) * seg_cap : nullptr;
   int st_n = 0;  // entries this wave found for its row (wave-uniform)
@@ -223,7 +227,7 @@ __global__ __launch_bounds__(kThreads, FP8 ? 4 : 1) void indexer_mfma(
           if (CAND && cand_row) {
             if constexpr (FP8) sacc *= ks_tile[buf][32 * nb + l32];
             sacc += 0.f;  // -0.0 -> +0.0
-            const bool hit = in && order_key(sacc) >= theta_k;
+            const bool hit = in && sacc >= theta_f;
             const uint64_t m = ballot(hit);
             if (m) {
               const int slot = st_n + lanes_below(m);
