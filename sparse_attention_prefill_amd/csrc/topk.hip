@@ -752,8 +752,18 @@ __global__ __launch_bounds__(512) void topk_theta_kernel(
     int nk, int max_vis, int K, int fuse_above, uint32_t* __restrict__ theta, int32_t* __restrict__ n_cand,
     int segs) {
   constexpr int kBytes = IdxOps<FP8>::kKeyBytes, kChunks = kBytes / 16;
-  __shared__ alignas(16) uint32_t hist[8][kThetaBins];
-  __shared__ alignas(16) unsigned char tile[128 * kBytes];
+  constexpr int kTileBytes = 128 * kBytes;                           // 16 KB (fp8) or 32 KB (bf16)
+  constexpr int kBufs = int(sizeof(uint32_t)) * 8 * kThetaBins / kTileBytes;  // 4 or 2
+  constexpr int kLoads = kTileBytes / (512 * 16);                   // direct loads per thread per tile
+  constexpr int kInFlight = kLoads + (FP8 ? 1 : 0);                  // per wave per tile (+ the scales)
+  static_assert(kBufs >= 2 && kBufs - 2 <= 2, "one to three tiles ahead");
+  // The sample tiles of the shared path live in the histogram's memory: the histograms are used
+  // only after the last tile.
+  __shared__ union {
+    alignas(16) uint32_t hist[8][kThetaBins];
+    alignas(16) unsigned char tiles[kBufs][kTileBytes];
+  } u;
+  __shared__ alignas(16) float ks_tiles[kBufs][FP8 ? 128 : 4];
   __shared__ int s_kv0[8], s_ev[8];
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -789,20 +799,48 @@ __global__ __launch_bounds__(512) void topk_theta_kernel(
   typename IdxOps<FP8>::AOp qa[2][IdxOps<FP8>::kKsteps];
   float wv[2][16];
   load_query_operands<FP8>(qi, w, q_scale, i, qa, wv);
+  // Wait here, visibly to the compiler, for the query operands (and the segment-count stores):
+  // the tiles below arrive by direct loads the compiler does not see, and a wait it placed at
+  // the first use of the operands would also drain them. vmcnt(0), other counters untouched.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+
+  auto tile_start = [&](int tl) { return int(int64_t(tl) * (ev_s - 128) / (kSampleTiles - 1)); };
+  // Shared path: tile tl goes to buffer tl % kBufs by direct global->LDS loads (the swizzled
+  // layout of key_operand_lds: slot (n, c) holds chunk kswz(n, c)), its key scales beside it
+  // (16 per wave).
+  auto issue_tile = [&](int tl) {
+    const int b = tl % kBufs, start = tile_start(tl);
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+      const int f0 = 64 * (kLoads * wave + j);  // this wave's 64 consecutive 16-byte slots
+      const int f = f0 + lane;
+      const int n = f / kChunks, c = kswz<kChunks>(n, f - n * kChunks);
+      lds_dma16_v(ki + int64_t(kv0 + start + n) * kBytes + c * 16, lds_offset(u.tiles[b] + f0 * 16));
+    }
+    if constexpr (FP8) {
+      if (lane < 16) lds_dma4_v(k_scale + kv0 + start + 16 * wave + lane, lds_offset(ks_tiles[b] + 16 * wave));
+    }
+  };
+  if (shared) {
+#pragma unroll
+    for (int tl = 0; tl < kBufs - 1; ++tl) issue_tile(tl);
+  }
   // block b = 4 * tile + sub covers positions start(tile) + 32 sub + [0, 32); lanes of half h keep
   // the keys of block 2p + h
   uint32_t sk[kSampleKeys / 64];
 #pragma unroll 1
   for (int tl = 0; tl < kSampleTiles; ++tl) {
-    const int start = int(int64_t(tl) * (ev_s - 128) / (kSampleTiles - 1));
+    const int start = tile_start(tl);
+    const int b = tl % kBufs;
     if (shared) {
-      __syncthreads();  // the previous tile is consumed
-      for (int f = tid; f < 128 * kChunks; f += 512) {
-        const int n = f / kChunks, c = f - n * kChunks;
-        *reinterpret_cast<i32x4*>(tile + n * kBytes + kswz<kChunks>(n, c) * 16) =
-            *reinterpret_cast<const i32x4*>(ki + int64_t(kv0 + start + n) * kBytes + c * 16);
-      }
-      __syncthreads();
+      // tile tl has landed for every wave (the tiles issued after it may stay in flight) and
+      // every wave is done with tile tl - 1, whose buffer takes tile tl + kBufs - 1
+      const int ahead = min(kSampleTiles - 1, tl + kBufs - 2) - tl;  // uniform, 0 .. kBufs - 2
+      static_assert(FP8 ? (kInFlight == 3 && kBufs == 4) : kBufs == 2, "the wait counts below are literals");
+      if (ahead >= 2) DSA_TILE_BARRIER_VMCNT(6);
+      else if (ahead == 1) DSA_TILE_BARRIER_VMCNT(3);
+      else DSA_TILE_BARRIER_VMCNT(0);
+      if (tl + kBufs - 1 < kSampleTiles) issue_tile(tl + kBufs - 1);
     }
 #pragma unroll
     for (int pp = 0; pp < 2; ++pp) {
@@ -812,22 +850,29 @@ __global__ __launch_bounds__(512) void topk_theta_kernel(
         const int n = 32 * (2 * pp + h) + l32;  // row in the tile
         const int row = kv0 + start + n;
         f32x16 a0, a1;
-        if (shared) block_mfma_chains<FP8>(qa, [&](int ks) { return key_operand_lds<FP8>(tile, n, ks); }, a0, a1);
-        else block_mfma_chains<FP8>(qa, [&](int ks) { return key_operand_global<FP8>(ki, row, ks); }, a0, a1);
-        float x = block_head_sum(wv, a0, a1);
-        if constexpr (FP8) x *= k_scale[row];
+        float x;
+        if (shared) {
+          block_mfma_chains<FP8>(qa, [&](int ks) { return key_operand_lds<FP8>(u.tiles[b], n, ks); }, a0, a1);
+          x = block_head_sum(wv, a0, a1);
+          if constexpr (FP8) x *= ks_tiles[b][n];
+        } else {
+          block_mfma_chains<FP8>(qa, [&](int ks) { return key_operand_global<FP8>(ki, row, ks); }, a0, a1);
+          x = block_head_sum(wv, a0, a1);
+          if constexpr (FP8) x *= k_scale[row];
+        }
         sc[h] = x + 0.f;
       }
       sk[2 * tl + pp] = order_key(half ? sc[1] : sc[0]);
     }
   }
+  if (shared) __syncthreads();  // every wave is done with the tiles before the histograms take their memory
   if (!cand) return;  // shared path: every wave is a candidate row; kept for clarity
 
   // r: smallest rank with r * ev / m - 5.5 sqrt(r) * ev / m >= K
   const double km = double(K) * kSampleKeys / ev;
   const double sr = 2.75 + sqrt(2.75 * 2.75 + km);
   const int r_s = int(min(double(kSampleKeys), ceil(sr * sr)));
-  uint32_t* h = hist[wave];
+  uint32_t* h = u.hist[wave];
   int bin1, bin2, rem, cnt;
   for (int b = 4 * lane; b < kThetaBins; b += 256) *reinterpret_cast<uint4*>(h + b) = uint4{0, 0, 0, 0};
   lds_wait();
