@@ -342,3 +342,32 @@ def test_attention_without_sink(name):
     assert np.all(np.isneginf(got_lse[2])) and np.all(np.isneginf(ref_lse[2]))
     live = np.arange(nq) != 2
     assert np.abs(got_lse[live] - ref_lse[live]).max() < (1e-4 if kind == "f32" else 2e-3)
+
+
+def test_attention_every_partial_tile_size():
+    """Query j selects j + 1 rows (1 .. 64) and a few more around two and three half-tiles, so the
+    last tile's mask is exercised at every fill level of both 32-row halves."""
+    dev = gpu()
+    import sparse_attention_prefill_amd as D
+    n_rows, k_tot = 400, 160
+    sizes = list(range(1, 65)) + [65, 95, 96, 97, 127, 128, 129, 160]
+    nq = len(sizes)
+    wl = S.WORKLOADS["inseq_cp8_last_8k"].with_(lens=(n_rows,))
+    inp = S.stream_inputs(wl, "unit")
+    qin = S.query_inputs(wl, np.arange(nq) * 5 % n_rows, "unit")
+    g = np.random.default_rng(11)
+    idx = np.full((nq, k_tot), -1, dtype=np.int32)
+    for j, n in enumerate(sizes):
+        slots = np.sort(g.permutation(k_tot)[:n])  # the -1 entries sit anywhere in the row
+        idx[j, slots] = g.permutation(n_rows)[:n]
+    scale = 1.0 / np.sqrt(wl.Dqk)
+    out = D.sparse_attn(to_dev(qin["q"], "bf16", dev), to_dev(inp["kv"], "bf16", dev), to_dev(idx, "i32", dev),
+                        to_dev(inp["sink"], "f32", dev), scale, wl.Dv)
+    torch.cuda.synchronize()
+    kv = O.decode(inp["kv"], "bf16")
+    sink = inp["sink"].astype(np.float64)
+    ref = np.stack([O.sparse_attention_row(O.decode(qin["q"][j], "bf16"), kv[idx[j][idx[j] >= 0]], sink, scale,
+                                           wl.Dv)[0] for j in range(nq)])
+    got = to_f64(out)
+    for j, n in enumerate(sizes):
+        assert_attn_close(got[j], ref[j], "bf16", f"{n} selected rows")
