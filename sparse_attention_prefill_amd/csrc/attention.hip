@@ -22,6 +22,8 @@
 //    inside fp32 / bf16 range); otherwise the workgroup sweeps the query's logits for their exact
 //    max and reruns it with that max.
 //  * sparse_attn_generic: float32 or bf16, small head counts (n_heads * d_v <= 4096); VALU.
+#include <atomic>
+
 #include "dsa_internal.h"
 
 namespace dsa {
@@ -523,18 +525,30 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
 
 size_t mla_attn_lds_bytes() { return 2 * kTileBytes + (kMaxKtot + kWaves + 2) * sizeof(int); }
 
+namespace {
+// Dynamic LDS above the default limit has to be allowed per kernel and per device: done once
+// per device (bit d of `done`; devices past 63 set it on every call). Safe from several threads.
+dsa_status allow_lds(const void* fn, int bytes, std::atomic<uint64_t>& done, const char* what) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return check_launch(what);
+  const uint64_t bit = dev >= 0 && dev < 64 ? (uint64_t(1) << dev) : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return DSA_OK;
+  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess)
+    return check_launch(what);
+  done.fetch_or(bit, std::memory_order_release);
+  return DSA_OK;
+}
+std::atomic<uint64_t> g_mla_lds{0};
+}  // namespace
+
 dsa_status launch_sparse_attn(const dsa_sparse_attn_args* a, hipStream_t stream) {
   if (a->nq == 0) return DSA_OK;
   const float scale_log2 = a->softmax_scale * kLog2e;
   if (a->dtype == DSA_BF16 && a->n_heads == kH && a->d_qk == kDqk && a->d_v == kDv) {
     if (a->k_tot > kMaxKtot) return fail(DSA_ERR_UNSUPPORTED, "sparse_attn: k_tot > 2304 for the MLA kernel");
-    static bool attr_set = false;
-    if (!attr_set) {
-      if (hipFuncSetAttribute(reinterpret_cast<const void*>(sparse_attn_mla_bf16),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, int(mla_attn_lds_bytes())) != hipSuccess)
-        return check_launch("hipFuncSetAttribute(sparse_attn_mla_bf16)");
-      attr_set = true;
-    }
+    const dsa_status st = allow_lds(reinterpret_cast<const void*>(sparse_attn_mla_bf16), int(mla_attn_lds_bytes()),
+                                    g_mla_lds, "hipFuncSetAttribute(sparse_attn_mla_bf16)");
+    if (st != DSA_OK) return st;
     hipLaunchKernelGGL(sparse_attn_mla_bf16, dim3(a->nq), dim3(kThreads), mla_attn_lds_bytes(), stream,
                        static_cast<const uint16_t*>(a->q), static_cast<const uint16_t*>(a->kv), a->idx, a->sink,
                        static_cast<uint16_t*>(a->out), a->lse, a->err_flag, scale_log2, a->n_rows, a->k_tot);
@@ -546,16 +560,19 @@ dsa_status launch_sparse_attn(const dsa_sparse_attn_args* a, hipStream_t stream)
   const size_t lds = sizeof(float) * (size_t(a->n_heads) * a->d_qk + size_t(kGenTile) * a->d_qk +
                                       size_t(a->n_heads) * kGenTile + 3 * size_t(a->n_heads)) +
                      sizeof(int) * kGenTile;
+  // the LDS size depends on the shape: allowed on every call
   if (a->dtype == DSA_F32) {
-    hipFuncSetAttribute(reinterpret_cast<const void*>(sparse_attn_generic<float>),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(sparse_attn_generic<float>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)) != hipSuccess)
+      return check_launch("hipFuncSetAttribute(sparse_attn_generic)");
     hipLaunchKernelGGL(sparse_attn_generic<float>, dim3(a->nq), dim3(kGenThreads), lds, stream,
                        static_cast<const float*>(a->q), static_cast<const float*>(a->kv), a->idx, a->sink,
                        static_cast<float*>(a->out), a->lse, a->err_flag, scale_log2, a->n_rows, a->n_heads,
                        a->d_qk, a->d_v, a->k_tot);
   } else if (a->dtype == DSA_BF16) {
-    hipFuncSetAttribute(reinterpret_cast<const void*>(sparse_attn_generic<uint16_t>),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(sparse_attn_generic<uint16_t>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)) != hipSuccess)
+      return check_launch("hipFuncSetAttribute(sparse_attn_generic)");
     hipLaunchKernelGGL(sparse_attn_generic<uint16_t>, dim3(a->nq), dim3(kGenThreads), lds, stream,
                        static_cast<const uint16_t*>(a->q), static_cast<const uint16_t*>(a->kv), a->idx, a->sink,
                        static_cast<uint16_t*>(a->out), a->lse, a->err_flag, scale_log2, a->n_rows, a->n_heads,
