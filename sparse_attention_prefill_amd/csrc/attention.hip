@@ -188,6 +188,24 @@ __device__ inline int rope_swz(int n) { return ((n >> 1) & 3) | (((n ^ (n >> 3))
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
+// Logit MFMAs with the accumulator in VGPRs. Every MFMA the compiler emits in this kernel takes
+// the AGPR form (the kernel needs AGPRs for O), and with O filling all 256 AGPRs the compiler
+// would move one O block out and back around every logit chain. Hazards are handled here: the
+// chain accumulates back to back into the same registers (as compiler-emitted chains do), the
+// first MFMA's result never shares registers with its operands (early clobber), the
+// memory clobber keeps the LDS operand reads where the source puts them (the compiler still
+// waits for each read before the asm that uses it), and logit_chain_done() pads the 8-pass
+// MFMA's result latency before any VALU may read the logits (it takes them as an operand).
+__device__ inline void logit_mfma_first(f32x16& s, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(a), "v"(b) : "memory");
+}
+__device__ inline void logit_mfma(f32x16& s, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(a), "v"(b) : "memory");
+}
+__device__ inline void logit_chain_done(f32x16& s) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 2" : "+v"(s)::"memory");  // 19 wait states
+}
+
 // ds_read_b64_tr_b16: inside each 16-lane group, lane o receives element o%4 of the 4-element
 // runs addressed by lanes 4j + o/4 (j = 0..3) -- a 16x4 -> 4x16 transpose.
 __device__ inline s16x4 lds_read_tr16(const unsigned char* p) {
@@ -390,7 +408,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) {  // 32-row halves of the tile
         // S^T[n][h] = K[n,:] . Q[h,:] for rows n = 32hb + 0..31
-        f32x16 s = f32x16{};
+        f32x16 s;
         if (hb == 0 && gather_next) {
           // explicit software pipeline: kLookK operand reads ahead; after every second MFMA one
           // gather load (its memory clobber keeps the operand reads in this order)
@@ -409,7 +427,8 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
             for (int u = 0; u < 2; ++u) {
               const int ks = 2 * c + u;
               if (ks + kLookK < kDqk / 16) a[ks + kLookK] = k_read(ks + kLookK);
-              s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], qreg[ks], s, 0, 0, 0);
+              if (ks == 0) logit_mfma_first(s, a[ks], qreg[ks]);
+              else logit_mfma(s, a[ks], qreg[ks]);
             }
             gather_one(gr, buf ^ 1, c);
           }
@@ -417,23 +436,23 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
           int r_x = r_x0;
           asm volatile("" : "+v"(r_x));  // recomputed per half-tile: no hoisting of the rope offsets
           bf16x8 a[kDqk / 16];
-#pragma unroll
-          for (int ks = 0; ks < kDv / 16; ++ks)
-            a[ks] = *reinterpret_cast<const bf16x8*>(tb + k_base + 32 * hb * kLatPitch + 32 * ks);
-#pragma unroll
-          for (int ks = kDv / 16; ks < kDqk / 16; ++ks)
-            a[ks] = *reinterpret_cast<const bf16x8*>(tb + r_base + ((32 * (ks - kDv / 16)) ^ r_x) + 32 * hb * kRopeBytes);
-#pragma unroll
-          for (int ks = 0; ks < kDqk / 16; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], qreg[ks], s, 0, 0, 0);
+          auto k_read = [&](int ks) {
+            return ks < kDv / 16
+                       ? *reinterpret_cast<const bf16x8*>(tb + k_base + 32 * hb * kLatPitch + 32 * ks)
+                       : *reinterpret_cast<const bf16x8*>(tb + r_base + ((32 * (ks - kDv / 16)) ^ r_x) +
+                                                          32 * hb * kRopeBytes);
+          };
           // issue order: kLookK operand reads ahead, then one MFMA per read
-          __builtin_amdgcn_sched_group_barrier(0x100, kLookK, 0);
 #pragma unroll
-          for (int ks = 0; ks < kDqk / 16 - kLookK; ++ks) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          for (int ks = 0; ks < kLookK; ++ks) a[ks] = k_read(ks);
+#pragma unroll
+          for (int ks = 0; ks < kDqk / 16; ++ks) {
+            if (ks + kLookK < kDqk / 16) a[ks + kLookK] = k_read(ks + kLookK);
+            if (ks == 0) logit_mfma_first(s, a[ks], qreg[ks]);
+            else logit_mfma(s, a[ks], qreg[ks]);
           }
-          __builtin_amdgcn_sched_group_barrier(0x008, kLookK, 0);
         }
+        logit_chain_done(s);
 
         // register v of the lane holds tile row 32hb + row_of_mfma_row(8(v/4) + 4half + v%4) =
         // 32hb + 16(v/8) + 4(v%4) + 2((v/4)%2) + half of head h; mask rows past the selection (only
