@@ -304,13 +304,12 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
                       rows[t * kTile + 16 * wave + 8 + (lane >> 3)]};
   };
   // load j (0..kLoadsPerWave-1) of this wave's share of the gather of a tile into buffer buf
+  const uint32_t lane16 = uint32_t(lane) << 4;  // every latent load's per-lane offset
   auto gather_one = [&](const GatherRows& gr, int buf, int j) {
-    int lane16 = lane << 4;
-    asm volatile("" : "+v"(lane16));  // keep per-lane offsets out of loop-invariant hoisting
     const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_offset(tiles + buf * kTileBytes));
     if (j < 16) {
       const int r = __builtin_amdgcn_readlane(gr.lat, j);
-      lds_dma16_s(kvb + int64_t(r) * kRowBytes, uint32_t(lane16), dst + uint32_t((16 * wave + j) * kLatPitch));
+      lds_dma16_s(kvb + int64_t(r) * kRowBytes, lane16, dst + uint32_t((16 * wave + j) * kLatPitch));
     } else {
       const int n0 = 16 * wave + 8 * (j - 16);  // rows n0 + lane/8
       const int c = (lane & 7) ^ rope_swz(n0 + (lane >> 3));
