@@ -158,6 +158,11 @@ constexpr int kLatTile = kTile * kLatPitch;        // 65 KiB
 constexpr int kTileBytes = kLatTile + kTile * kRopeBytes;  // 73 KiB
 constexpr int kMaxKtot = 2304;                     // selected rows per query held in LDS (9 KiB)
 constexpr int kLoadsPerWave = 18;                  // 16 latent rows + 2 rope instructions
+// Q staging: 32 head rows per wave at a pitch of 1168 bytes (73 chunks of 16: the row, then one
+// pad chunk), so the 16 lanes of one 16-byte operand read fall on 16 distinct bank groups
+constexpr int kQPitch = kRowBytes + 16, kQChunks = kQPitch / 16;
+constexpr int kQLoads = (32 * kQChunks + 63) / 64;  // 1 KiB direct loads per wave (37)
+static_assert(kWaves * 32 * kQPitch <= 2 * kTileBytes, "Q staging fits in the tile buffers");
 static_assert(kDqk / 32 == kLoadsPerWave, "one gather load per two logit MFMAs of a half-tile");
 #ifndef DSA_LOOKK
 #define DSA_LOOKK 3
@@ -187,6 +192,7 @@ __device__ inline int row_of_mfma_row(int m) {
 __device__ inline int rope_swz(int n) { return ((n >> 1) & 3) | (((n ^ (n >> 3)) & 1) << 2); }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 // Logit MFMAs with the accumulator in VGPRs. Every MFMA the compiler emits in this kernel takes
 // the AGPR form (the kernel needs AGPRs for O), and with O filling all 256 AGPRs the compiler
@@ -212,20 +218,29 @@ __device__ inline s16x4 lds_read_tr16(const unsigned char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
 }
 
-// Selected row ids of query i -> rows[], validated (-1 skipped, out-of-range flagged and
-// skipped) and compacted in order; the tail up to a multiple of `tile` is padded with row 0 (a
-// valid row whose logits are masked). Returns the number of selected rows. All threads call it.
-__device__ inline int compact_rows(const int32_t* __restrict__ idx, int i, int k_tot, int n_rows, int tile, int* rows,
-                                   int* scan, int32_t* err_flag) {
-  constexpr int kPer = kMaxKtot / kThreads;  // 9 entries per thread
+constexpr int kSelPer = kMaxKtot / kThreads;  // selection entries per thread (9)
+
+// This thread's share of query i's selected row ids: entries kSelPer*tid .. +kSelPer (-1 past k_tot)
+__device__ inline void load_selection(const int32_t* __restrict__ idx, int i, int k_tot, int (&vals)[kSelPer]) {
+#pragma unroll
+  for (int k = 0; k < kSelPer; ++k) {
+    const int e = threadIdx.x * kSelPer + k;
+    vals[k] = e < k_tot ? idx[int64_t(i) * k_tot + e] : -1;
+  }
+}
+
+// Selected row ids (from load_selection) -> rows[], validated (-1 skipped, out-of-range flagged
+// and skipped) and compacted in order; the tail up to a multiple of `tile` is padded with row 0
+// (a valid row whose logits are masked). Returns the number of selected rows. All threads call it.
+__device__ inline int compact_rows(int (&vals)[kSelPer], int n_rows, int tile, int* rows, int* scan,
+                                   int32_t* err_flag) {
+  constexpr int kPer = kSelPer;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int vals[kPer];
   int cnt = 0;
   bool bad = false;
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
-    const int e = tid * kPer + k;
-    int r = e < k_tot ? idx[int64_t(i) * k_tot + e] : -1;
+    int r = vals[k];
     if (r < -1 || r >= n_rows) {
       bad = true;
       r = -1;
@@ -277,17 +292,34 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
   const int half = lane >> 5, l32 = lane & 31;
   const int h = wave * 32 + l32;  // this lane's head in S^T / softmax
 
-  const int n_sel = compact_rows(idx, i, k_tot, n_rows, kTile, rows, scan, err_flag);
-
-  const int n_tiles = (n_sel + kTile - 1) / kTile;
-
   // ---- Q^T operand for S^T = K Q^T: lane holds q[h, 16ks + 8half .. +8) ----
-  bf16x8 qreg[kDqk / 16];
+  // Staged through the (still unused) tile buffers: wave w copies its 32 head rows, contiguous in
+  // HBM, with 1 KiB direct loads into rows of kQPitch bytes, and each lane then reads its operand
+  // 16 bytes at a time. (Loading the operand straight into registers fetches every 128-byte line
+  // in four 32-byte pieces, 32 lines per instruction, at a fraction of the CU's load rate.)
+  // The staging copy, the selection loads and the compaction overlap.
+  unsigned char* qstage = tiles + wave * 32 * kQPitch;
   {
-    const bf16x8* qp = reinterpret_cast<const bf16x8*>(q + (int64_t(i) * kH + h) * kDqk) + half;
+    const unsigned char* qrows = reinterpret_cast<const unsigned char*>(q + (int64_t(i) * kH + wave * 32) * kDqk);
+    const uint32_t dst = lds_offset(qstage);
 #pragma unroll
-    for (int ks = 0; ks < kDqk / 16; ++ks) qreg[ks] = qp[2 * ks];
+    for (int j = 0; j < kQLoads; ++j) {
+      const int c = 64 * j + lane;  // 16-byte chunk of the staging rows: row c / 73, chunk c % 73
+      const int r = c / kQChunks, col = c % kQChunks;
+      const uint32_t src = uint32_t(r * kRowBytes + 16 * (col < kQChunks - 1 ? col : 0));  // pad: any chunk
+      if (c < 32 * kQChunks) lds_dma16_s(qrows, src, dst + 1024 * j);
+    }
   }
+  int sel[kSelPer];
+  load_selection(idx, i, k_tot, sel);
+  const int n_sel = compact_rows(sel, n_rows, kTile, rows, scan, err_flag);
+  const int n_tiles = (n_sel + kTile - 1) / kTile;
+  bf16x8 qreg[kDqk / 16];
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's staging rows have landed
+#pragma unroll
+  for (int ks = 0; ks < kDqk / 16; ++ks)
+    qreg[ks] = *reinterpret_cast<const bf16x8*>(qstage + l32 * kQPitch + 32 * ks + 16 * half);
+  DSA_TILE_BARRIER_LDS();  // every wave holds its operand before the first gather reuses the space
 
   // ---- gather of one tile into LDS with direct global->LDS loads ----
   //  latent: instruction j of this wave moves row n = 16*wave + j (one uniform row id, 64 lanes x
@@ -335,11 +367,12 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
   const int r_base = kLatTile + k_row * kRopeBytes, r_x0 = (half ^ rope_swz(k_row)) << 4;
   const int v_base = (4 * ((lane & 15) >> 2) + half) * kLatPitch + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
 
-  const float sink_l2 = sink ? sink[h] * kLog2e : -INFINITY;
   f32x16 oacc[kDv / 32];
   float m_used = -INFINITY, l_run = 0.f, m_seen = -INFINITY;
   if (tid == 0) *redo_flag = 0;
-  // Wait here, visibly to the compiler, for the Q^T loads (and the sink load). The tile
+  if (n_tiles > 0) issue_tile(0, 0);  // the first pass's first tile
+  const float sink_l2 = sink ? sink[h] * kLog2e : -INFINITY;
+  // Wait here, visibly to the compiler, for the sink load (and the first tile). The tile
   // barriers are inline asm the compiler does not see through; without this it would place
   // graded vmcnt waits before the first MFMAs of every tile, which also drain the next tile's
   // gather loads. Encoding: vmcnt(0), expcnt and lgkmcnt left at their maximum.
@@ -390,7 +423,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
 #pragma unroll
     for (int db = 0; db < kDv / 32; ++db) oacc[db] = f32x16{};
 
-    if (n_tiles > 0) issue_tile(0, 0);
+    if (attempt == 1 && n_tiles > 0) issue_tile(0, 0);
     for (int t = 0; t < n_tiles; ++t) {
       const int buf = t & 1;
       // One barrier per tile: after it, this tile has landed for every wave AND every wave has
@@ -487,8 +520,10 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
         psum = xor32_sum(psum);
         l_run += psum;
 
-        // O[h][d] += P[h][n] V[n][d]; k-slot 8half + jj of step kk is the S^T row of register
-        // 8kk + jj: tile row 32hb + 16kk + 4(jj%4) + 2(jj/4) + half
+        // O^T[d][h] += V^T[d][n] P^T[n][h] (V as the A operand, P as B: the same registers as
+        // for O = P V, which would leave a lane one column of 16 heads; O^T leaves it 16 columns
+        // of its own head); k-slot 8half + jj of step kk is the S^T row of register 8kk + jj:
+        // tile row 32hb + 16kk + 4(jj%4) + 2(jj/4) + half
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
           const unsigned char* vb = tb + v_base + (32 * hb + 16 * kk) * kLatPitch;
@@ -501,7 +536,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
 #pragma unroll
           for (int db = 0; db < kDv / 32; ++db) {
             const s16x8 vv = s16x8{lo[db][0], lo[db][1], lo[db][2], lo[db][3], hi[db][0], hi[db][1], hi[db][2], hi[db][3]};
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[kk], __builtin_bit_cast(bf16x8, vv), oacc[db],
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pa[kk], oacc[db],
                                                                 0, 0, 0);
           }
           __builtin_amdgcn_sched_group_barrier(0x100, 2 * kLookV, 0);
@@ -524,17 +559,29 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
     }
   }
 
-  // ---- normalise and store: lane holds d = 32db + l32 for heads 8(v/4) + 4half + v%4 ----
+  // ---- normalise and store: oacc[db][4g + c] = O[h][32db + 8g + 4half + c] ----
+  // Each wave stages its 32 x 512 block in LDS (row pitch 1040: the lanes of one 8-byte write hit
+  // every bank once per 32 lanes) and writes whole 1 KiB output rows with 16-byte stores.
+  __syncthreads();  // every wave is done with the tile buffers
   const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+  constexpr int kOutPitch = kDv * 2 + 16;
+  static_assert(kWaves * 32 * kOutPitch <= 2 * kTileBytes, "output staging fits in the tile buffers");
+  unsigned char* stage = tiles + wave * 32 * kOutPitch;
+#pragma unroll
+  for (int db = 0; db < kDv / 32; ++db) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      bf16x4 o;  // round to nearest even (the hardware conversion)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) o[c] = (__bf16)(oacc[db][4 * g + c] * inv);
+      *reinterpret_cast<bf16x4*>(stage + l32 * kOutPitch + 2 * (32 * db + 8 * g + 4 * half)) = o;
+    }
+  }
+  asm volatile("" ::: "memory");  // the wave reads back what its own lanes wrote (LDS keeps order)
   uint16_t* op = out + (int64_t(i) * kH + wave * 32) * kDv;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int hl = 8 * (v >> 2) + 4 * half + (v & 3);
-    const float iv = __shfl(inv, hl, 64);
-#pragma unroll
-    for (int db = 0; db < kDv / 32; ++db)  // round to nearest even (the hardware conversion)
-      op[hl * kDv + 32 * db + l32] = __builtin_bit_cast(uint16_t, (__bf16)(oacc[db][v] * iv));
-  }
+  for (int r = 0; r < 32; ++r)
+    *reinterpret_cast<bf16x8*>(op + r * kDv + 8 * lane) = *reinterpret_cast<const bf16x8*>(stage + r * kOutPitch + 16 * lane);
   if (lse && half == 0) lse[int64_t(i) * kH + h] = l_run > 0.f ? (m_used + log2f(l_run)) / kLog2e : -INFINITY;
 }
 
