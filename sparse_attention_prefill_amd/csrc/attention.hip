@@ -296,8 +296,9 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
   // Staged through the (still unused) tile buffers: wave w copies its 32 head rows, contiguous in
   // HBM, with 1 KiB direct loads into rows of kQPitch bytes, and each lane then reads its operand
   // 16 bytes at a time. (Loading the operand straight into registers fetches every 128-byte line
-  // in four 32-byte pieces, 32 lines per instruction, at a fraction of the CU's load rate.)
-  // The staging copy, the selection loads and the compaction overlap.
+  // in four 32-byte pieces, 32 lines per instruction.) The selection loads are issued behind the
+  // copy; the compaction's wait for them is a full vmcnt wait (the compiler does not count the
+  // direct loads), so it also covers the copy.
   unsigned char* qstage = tiles + wave * 32 * kQPitch;
   {
     const unsigned char* qrows = reinterpret_cast<const unsigned char*>(q + (int64_t(i) * kH + wave * 32) * kDqk);
