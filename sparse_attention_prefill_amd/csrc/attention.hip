@@ -48,15 +48,25 @@ template <> __device__ inline void store_elt<uint16_t>(uint16_t* p, int64_t i, f
   p[i] = float_to_bf16_bits(v);
 }
 
+// LDS row pitch (floats) of the generic kernel's Q and KV rows: a whole number of 16-byte chunks,
+// and an odd one, so the 16-byte reads of 16 consecutive rows fall on 16 distinct bank groups.
+// The pad columns hold zeros.
+__host__ __device__ constexpr int gen_pitch(int d) {
+  const int p = (d + 3) / 4 * 4;
+  return (p / 4) % 2 == 0 ? p + 4 : p;
+}
+static_assert(kGenThreads % kGenTile == 0 && kGenTile == 32, "a head's logits of a tile are 32 lanes of one wave");
+
 template <typename T>
 __global__ __launch_bounds__(kGenThreads) void sparse_attn_generic(
     const T* __restrict__ q, const T* __restrict__ kv, const int32_t* __restrict__ idx,
     const float* __restrict__ sink, T* __restrict__ out, float* __restrict__ lse, int32_t* __restrict__ err_flag,
     float scale_log2, int n_rows, int H, int Dqk, int Dv, int k_tot) {
-  extern __shared__ float smem[];
-  float* sq = smem;                          // [H, Dqk]
-  float* skv = sq + H * Dqk;                 // [kGenTile, Dqk]
-  float* sl = skv + kGenTile * Dqk;          // [H, kGenTile] logits -> probabilities
+  extern __shared__ __attribute__((aligned(16))) float smem[];
+  const int P = gen_pitch(Dqk), n4 = P / 4;
+  float* sq = smem;                          // [H, P]
+  float* skv = sq + H * P;                   // [kGenTile, P]
+  float* sl = skv + kGenTile * P;            // [H, kGenTile] probabilities of the tile
   float* sm = sl + H * kGenTile;             // [H] running max (log2 units)
   float* ssum = sm + H;                      // [H] running denominator
   float* salpha = ssum + H;                  // [H] rescale factor of this tile
@@ -64,7 +74,10 @@ __global__ __launch_bounds__(kGenThreads) void sparse_attn_generic(
 
   const int i = blockIdx.x;
   const int tid = threadIdx.x;
-  for (int e = tid; e < H * Dqk; e += kGenThreads) sq[e] = load_elt(q, int64_t(i) * H * Dqk + e);
+  for (int e = tid; e < H * P; e += kGenThreads) {
+    const int h = e / P, d = e - h * P;
+    sq[e] = d < Dqk ? load_elt(q, (int64_t(i) * H + h) * Dqk + d) : 0.f;
+  }
   for (int h = tid; h < H; h += kGenThreads) {
     sm[h] = sink ? sink[h] * kLog2e : -INFINITY;
     ssum[h] = sink ? 1.f : 0.f;
@@ -85,36 +98,48 @@ __global__ __launch_bounds__(kGenThreads) void sparse_attn_generic(
       srow[tid] = r;
     }
     __syncthreads();
-    for (int e = tid; e < kGenTile * Dqk; e += kGenThreads) {
-      const int rr = e / Dqk, d = e - rr * Dqk;
+    for (int e = tid; e < kGenTile * P; e += kGenThreads) {
+      const int rr = e / P, d = e - rr * P;
       const int r = srow[rr];
-      skv[e] = r >= 0 ? load_elt(kv, int64_t(r) * Dqk + d) : 0.f;
+      skv[e] = r >= 0 && d < Dqk ? load_elt(kv, int64_t(r) * Dqk + d) : 0.f;
     }
     __syncthreads();
+    // Logits and the online softmax. Lane e holds (head e / 32, tile row e % 32): the 32 rows of a
+    // head are 32 lanes of one wave, so its max and sum are lane reductions; the lane of row 0
+    // updates the head's running max, denominator and rescale factor.
     for (int e = tid; e < H * kGenTile; e += kGenThreads) {
       const int h = e / kGenTile, rr = e - h * kGenTile;
       float s = -INFINITY;
       if (srow[rr] >= 0) {
+        const float4* a = reinterpret_cast<const float4*>(sq + h * P);
+        const float4* b = reinterpret_cast<const float4*>(skv + rr * P);
         float dot = 0.f;
-        for (int d = 0; d < Dqk; ++d) dot = fmaf(sq[h * Dqk + d], skv[rr * Dqk + d], dot);
+#pragma unroll 4
+        for (int d4 = 0; d4 < n4; ++d4) {
+          const float4 x = a[d4], y = b[d4];
+          dot = fmaf(x.x, y.x, dot);
+          dot = fmaf(x.y, y.y, dot);
+          dot = fmaf(x.z, y.z, dot);
+          dot = fmaf(x.w, y.w, dot);
+        }
         s = dot * scale_log2;
       }
-      sl[e] = s;
-    }
-    __syncthreads();
-    for (int h = tid; h < H; h += kGenThreads) {
-      float mx = sm[h];
-      for (int rr = 0; rr < kGenTile; ++rr) mx = fmaxf(mx, sl[h * kGenTile + rr]);
-      const float alpha = mx == -INFINITY ? 1.f : exp2f(sm[h] - mx);
-      float sum = ssum[h] * alpha;
-      for (int rr = 0; rr < kGenTile; ++rr) {
-        const float p = mx == -INFINITY ? 0.f : exp2f(sl[h * kGenTile + rr] - mx);
-        sl[h * kGenTile + rr] = p;
-        sum += p;
+      float mx = s;
+#pragma unroll
+      for (int o = kGenTile / 2; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kGenTile));
+      const float m_old = sm[h];
+      const float m_new = fmaxf(m_old, mx);
+      const float pr = m_new == -INFINITY ? 0.f : exp2f(s - m_new);
+      float sum = pr;
+#pragma unroll
+      for (int o = kGenTile / 2; o > 0; o >>= 1) sum += __shfl_xor(sum, o, kGenTile);
+      sl[e] = pr;
+      if (rr == 0) {
+        const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_old - m_new);
+        sm[h] = m_new;
+        ssum[h] = ssum[h] * alpha + sum;
+        salpha[h] = alpha;
       }
-      sm[h] = mx;
-      ssum[h] = sum;
-      salpha[h] = alpha;
     }
     __syncthreads();
     for (int k = 0; k < kMaxPer; ++k) {
@@ -122,7 +147,7 @@ __global__ __launch_bounds__(kGenThreads) void sparse_attn_generic(
       if (e < H * Dv) {
         const int h = e / Dv, d = e - h * Dv;
         float a = acc[k] * salpha[h];
-        for (int rr = 0; rr < kGenTile; ++rr) a = fmaf(sl[h * kGenTile + rr], skv[rr * Dqk + d], a);
+        for (int rr = 0; rr < kGenTile; ++rr) a = fmaf(sl[h * kGenTile + rr], skv[rr * P + d], a);
         acc[k] = a;
       }
     }
@@ -626,7 +651,8 @@ dsa_status launch_sparse_attn(const dsa_sparse_attn_args* a, hipStream_t stream)
   // generic kernel
   if (a->n_heads * a->d_v > 4096 || a->d_qk > 512 || a->n_heads * a->d_qk > 16384)
     return fail(DSA_ERR_UNSUPPORTED, "sparse_attn: shape not supported by the generic kernel");
-  const size_t lds = sizeof(float) * (size_t(a->n_heads) * a->d_qk + size_t(kGenTile) * a->d_qk +
+  const size_t pitch = size_t(gen_pitch(a->d_qk));
+  const size_t lds = sizeof(float) * (size_t(a->n_heads) * pitch + size_t(kGenTile) * pitch +
                                       size_t(a->n_heads) * kGenTile + 3 * size_t(a->n_heads)) +
                      sizeof(int) * kGenTile;
   // the LDS size depends on the shape: allowed on every call

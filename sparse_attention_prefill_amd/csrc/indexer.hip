@@ -39,8 +39,20 @@ constexpr int kGenThreads = 256;
 template <typename T> __device__ inline float ld_elt(const T* p, int64_t i);
 template <> __device__ inline float ld_elt<float>(const float* p, int64_t i) { return p[i]; }
 template <> __device__ inline float ld_elt<uint16_t>(const uint16_t* p, int64_t i) { return bf16_bits_to_float(p[i]); }
+// elements i .. i + 3 (i a multiple of 4, the buffer 16-byte aligned) in one load
+template <typename T> __device__ inline float4 ld_elt4(const T* p, int64_t i);
+template <> __device__ inline float4 ld_elt4<float>(const float* p, int64_t i) {
+  return *reinterpret_cast<const float4*>(p + i);
+}
+template <> __device__ inline float4 ld_elt4<uint16_t>(const uint16_t* p, int64_t i) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p + i);
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u), __uint_as_float(u.y << 16),
+                     __uint_as_float(u.y & 0xFFFF0000u));
+}
 
-template <typename T>
+// KD > 0: key rows of D <= KD elements (D a multiple of 4) are read once into registers; otherwise
+// every head reads the row from memory again. Same arithmetic, in the same order, either way.
+template <typename T, int KD>
 __global__ __launch_bounds__(kGenThreads) void indexer_generic(
     const T* __restrict__ qi, const float* __restrict__ w, const T* __restrict__ ki, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ used_kv, const int32_t* __restrict__ cu_kv, int batch, int stride, int ratio,
@@ -63,10 +75,29 @@ __global__ __launch_bounds__(kGenThreads) void indexer_generic(
   if (s >= ev) return;
   const int64_t krow = int64_t(v.kv0 + s) * D;
   float acc = 0.f;
-  for (int h = 0; h < H; ++h) {
-    float dot = 0.f;
-    for (int d = 0; d < D; ++d) dot = fmaf(sq[h * D + d], ld_elt(ki, krow + d), dot);
-    acc = fmaf(sq[H * D + h], fmaxf(dot, 0.f), acc);
+  if constexpr (KD > 0) {
+    float kr[KD];
+#pragma unroll
+    for (int d = 0; d < KD; d += 4) {
+      const float4 x = d < D ? ld_elt4(ki, krow + d) : make_float4(0.f, 0.f, 0.f, 0.f);
+      kr[d] = x.x;
+      kr[d + 1] = x.y;
+      kr[d + 2] = x.z;
+      kr[d + 3] = x.w;
+    }
+    for (int h = 0; h < H; ++h) {
+      float dot = 0.f;
+#pragma unroll
+      for (int d = 0; d < KD; ++d)
+        if (d < D) dot = fmaf(sq[h * D + d], kr[d], dot);
+      acc = fmaf(sq[H * D + h], fmaxf(dot, 0.f), acc);
+    }
+  } else {
+    for (int h = 0; h < H; ++h) {
+      float dot = 0.f;
+      for (int d = 0; d < D; ++d) dot = fmaf(sq[h * D + d], ld_elt(ki, krow + d), dot);
+      acc = fmaf(sq[H * D + h], fmaxf(dot, 0.f), acc);
+    }
   }
   scores[int64_t(i) * ld + s] = acc + 0.f;  // -0.0 -> +0.0
 }
@@ -305,19 +336,25 @@ dsa_status launch_indexer_scores(const dsa_indexer_topk_args* a, float* scores, 
     return fail(DSA_ERR_UNSUPPORTED, "indexer: shape not supported by the generic kernel");
   const dim3 grid((max_vis + kGenThreads - 1) / kGenThreads, a->nq);
   const size_t lds = sizeof(float) * (size_t(a->n_heads) * a->head_dim + a->n_heads);
+  const int D = a->head_dim;
+  const int kd = D % 4 != 0 ? 0 : D <= 32 ? 32 : D <= 64 ? 64 : 0;  // key-row register cache
+#define DSA_GEN_IDX(T, KD)                                                                                    \
+  hipLaunchKernelGGL((indexer_generic<T, KD>), grid, dim3(kGenThreads), lds, stream,                         \
+                     static_cast<const T*>(a->q_idx), a->weights, static_cast<const T*>(a->k_idx), a->cu_seqlens_q, \
+                     a->seqused_kv, a->cu_seqlens_kv, a->batch, stride, ratio, a->nq, a->nk, a->n_heads, D, max_vis, \
+                     skip_le, scores, ld, a->err_flag)
   if (a->dtype == DSA_F32) {
-    hipLaunchKernelGGL(indexer_generic<float>, grid, dim3(kGenThreads), lds, stream,
-                       static_cast<const float*>(a->q_idx), a->weights, static_cast<const float*>(a->k_idx),
-                       a->cu_seqlens_q, a->seqused_kv, a->cu_seqlens_kv, a->batch, stride, ratio, a->nq, a->nk,
-                       a->n_heads, a->head_dim, max_vis, skip_le, scores, ld, a->err_flag);
+    if (kd == 32) DSA_GEN_IDX(float, 32);
+    else if (kd == 64) DSA_GEN_IDX(float, 64);
+    else DSA_GEN_IDX(float, 0);
   } else if (a->dtype == DSA_BF16) {
-    hipLaunchKernelGGL(indexer_generic<uint16_t>, grid, dim3(kGenThreads), lds, stream,
-                       static_cast<const uint16_t*>(a->q_idx), a->weights, static_cast<const uint16_t*>(a->k_idx),
-                       a->cu_seqlens_q, a->seqused_kv, a->cu_seqlens_kv, a->batch, stride, ratio, a->nq, a->nk,
-                       a->n_heads, a->head_dim, max_vis, skip_le, scores, ld, a->err_flag);
+    if (kd == 32) DSA_GEN_IDX(uint16_t, 32);
+    else if (kd == 64) DSA_GEN_IDX(uint16_t, 64);
+    else DSA_GEN_IDX(uint16_t, 0);
   } else {
     return fail(DSA_ERR_UNSUPPORTED, "indexer: unknown dtype");
   }
+#undef DSA_GEN_IDX
   return check_launch("indexer_generic");
 }
 
