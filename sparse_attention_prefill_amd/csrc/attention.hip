@@ -42,6 +42,16 @@ template <> __device__ inline float load_elt<float>(const float* p, int64_t i) {
 template <> __device__ inline float load_elt<uint16_t>(const uint16_t* p, int64_t i) {
   return bf16_bits_to_float(p[i]);
 }
+// elements i .. i + 3 in one load (i a multiple of 4 of a 16-byte aligned buffer)
+template <typename T> __device__ inline float4 load_elt4(const T* p, int64_t i);
+template <> __device__ inline float4 load_elt4<float>(const float* p, int64_t i) {
+  return *reinterpret_cast<const float4*>(p + i);
+}
+template <> __device__ inline float4 load_elt4<uint16_t>(const uint16_t* p, int64_t i) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p + i);
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u), __uint_as_float(u.y << 16),
+                     __uint_as_float(u.y & 0xFFFF0000u));
+}
 template <typename T> __device__ inline void store_elt(T* p, int64_t i, float v);
 template <> __device__ inline void store_elt<float>(float* p, int64_t i, float v) { p[i] = v; }
 template <> __device__ inline void store_elt<uint16_t>(uint16_t* p, int64_t i, float v) {
@@ -74,13 +84,27 @@ __global__ __launch_bounds__(kGenThreads) void sparse_attn_generic(
 
   const int i = blockIdx.x;
   const int tid = threadIdx.x;
-  for (int e = tid; e < H * P; e += kGenThreads) {
-    const int h = e / P, d = e - h * P;
-    sq[e] = d < Dqk ? load_elt(q, (int64_t(i) * H + h) * Dqk + d) : 0.f;
+  if (Dqk % 4 == 0) {  // 4 elements per load; the pad chunk (if any) is zeroed
+    const int c4 = P / 4, n = H * c4;
+#pragma unroll 4
+    for (int e = tid; e < n; e += kGenThreads) {
+      const int h = e / c4, c = e - h * c4;
+      *reinterpret_cast<float4*>(sq + h * P + 4 * c) =
+          4 * c < Dqk ? load_elt4(q, (int64_t(i) * H + h) * Dqk + 4 * c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  } else {
+    for (int e = tid; e < H * P; e += kGenThreads) {
+      const int h = e / P, d = e - h * P;
+      sq[e] = d < Dqk ? load_elt(q, (int64_t(i) * H + h) * Dqk + d) : 0.f;
+    }
   }
   for (int h = tid; h < H; h += kGenThreads) {
     sm[h] = sink ? sink[h] * kLog2e : -INFINITY;
     ssum[h] = sink ? 1.f : 0.f;
+  }
+  for (int e = tid; e < kGenTile * (P - Dqk); e += kGenThreads) {
+    const int rr = e / (P - Dqk);
+    skv[rr * P + Dqk + (e - rr * (P - Dqk))] = 0.f;
   }
   constexpr int kMaxPer = 4096 / kGenThreads;  // H*Dv <= 4096
   float acc[kMaxPer];
@@ -98,10 +122,36 @@ __global__ __launch_bounds__(kGenThreads) void sparse_attn_generic(
       srow[tid] = r;
     }
     __syncthreads();
-    for (int e = tid; e < kGenTile * P; e += kGenThreads) {
-      const int rr = e / P, d = e - rr * P;
-      const int r = srow[rr];
-      skv[e] = r >= 0 && d < Dqk ? load_elt(kv, int64_t(r) * Dqk + d) : 0.f;
+    if (Dqk % 4 == 0) {
+      // 4 elements per load, all of a thread's loads issued before any is stored (the pad
+      // columns, zeroed before the first tile, are never written)
+      constexpr int kIt = kGenTile * (512 / 4) / kGenThreads;  // Dqk <= 512
+      const int c4 = Dqk / 4, n = kGenTile * c4;
+      float4 x[kIt];
+#pragma unroll
+      for (int k = 0; k < kIt; ++k) {
+        const int e = tid + k * kGenThreads;
+        x[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (e < n) {
+          const int rr = e / c4, c = e - rr * c4;
+          const int r = srow[rr];
+          if (r >= 0) x[k] = load_elt4(kv, int64_t(r) * Dqk + 4 * c);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < kIt; ++k) {
+        const int e = tid + k * kGenThreads;
+        if (e < n) {
+          const int rr = e / c4, c = e - rr * c4;
+          *reinterpret_cast<float4*>(skv + rr * P + 4 * c) = x[k];
+        }
+      }
+    } else {
+      for (int e = tid; e < kGenTile * P; e += kGenThreads) {
+        const int rr = e / P, d = e - rr * P;
+        const int r = srow[rr];
+        skv[e] = r >= 0 && d < Dqk ? load_elt(kv, int64_t(r) * Dqk + d) : 0.f;
+      }
     }
     __syncthreads();
     // Logits and the online softmax. Lane e holds (head e / 32, tile row e % 32): the 32 rows of a
