@@ -159,6 +159,15 @@ def test_indexer_scores(name, kw, variant):
     _indexer_case(S.WORKLOADS[name].with_(**kw), variant, dev)
 
 
+# Head dimensions that take the generic indexer's other paths: not a multiple of 4 or over 64
+# (key rows re-read per head), 48 (held in registers, a 64-slot row with the tail unused), and
+# bf16 rows of 64 read 4 elements at a time.
+@pytest.mark.parametrize("Hi,Di,kind", [(4, 30, "f32"), (2, 100, "f32"), (4, 48, "f32"), (8, 64, "bf16")])
+def test_generic_indexer_shapes(Hi, Di, kind):
+    wl = S.WORKLOADS["tiny_fp32_cp1"].with_(lens=(300,), Hi=Hi, Di=Di, idx_dtype=kind)
+    _indexer_case(wl, "normal", gpu())
+
+
 def _rand_idx(g, nq, k_tot, n_rows, frac_missing=0.1, empty_rows=()):
     idx = g.integers(0, n_rows, size=(nq, k_tot)).astype(np.int32)
     idx[g.random((nq, k_tot)) < frac_missing] = -1
@@ -177,9 +186,22 @@ def _rand_idx(g, nq, k_tot, n_rows, frac_missing=0.1, empty_rows=()):
     ("inseq_cp8_last_8k", 4, 1, 3),
 ])
 def test_attention_on_given_sets(name, nq, k_tot, n_rows, variant):
+    _attention_case(S.WORKLOADS[name].with_(lens=(n_rows,)), nq, k_tot, n_rows, variant)
+
+
+# Shapes that take the generic kernel's other load paths: a head dimension that is not a multiple
+# of 4 (element loads, zeroed pad columns), bf16 rows loaded 4 elements at a time, and the largest
+# head dimension the kernel accepts (a tile's loads fill every slot of the per-thread batch).
+@pytest.mark.parametrize("H,Dqk,Dv,dtype", [(8, 70, 64, "f32"), (16, 160, 128, "bf16"), (8, 512, 256, "f32")])
+def test_generic_attention_shapes(H, Dqk, Dv, dtype):
+    wl = S.WORKLOADS["tiny_fp32_cp1"].with_(lens=(300,), H=H, Dqk=Dqk, Dv=Dv, attn_dtype=dtype)
+    _attention_case(wl, 11, 70, 300, "normal")
+
+
+def _attention_case(wl, nq, k_tot, n_rows, variant):
     dev = gpu()
     import sparse_attention_prefill_amd as D
-    wl = S.WORKLOADS[name].with_(lens=(n_rows,))
+    name = wl.name
     inp = S.stream_inputs(wl, variant)
     qin = S.query_inputs(wl, np.arange(nq) * 7 % n_rows, variant)
     g = np.random.default_rng(nq * 1000 + k_tot)
