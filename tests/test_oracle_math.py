@@ -200,22 +200,36 @@ def test_attention_set_semantics_and_empty_set():
 
 
 def test_attention_value_columns_are_the_leading_ones():
-    q, kv, sink, Dv = _rand_attn(23, n=5, D=10, Dv=4)
-    kv2 = kv.copy()
-    kv2[:, Dv:] *= 0   # changes the logits only
-    o, _ = O.sparse_attention_row(q, kv, sink, 0.3, Dv)
-    kv3 = kv.copy()
-    kv3[:, :Dv] *= 2   # changes the logits and doubles the values
-    o3, _ = O.sparse_attention_row(q / 1.0, kv3, sink, 0.3, Dv)
-    assert o.shape == (3, 4)
-    assert not np.allclose(o, O.sparse_attention_row(q, kv2, sink, 0.3, Dv)[0])
-    assert not np.allclose(o3, 2 * o)
+    """V = the first D_v columns; the logit uses every D_qk column (R-11). Hand-worked values."""
+    kv = np.array([[1.0, 2.0, 3.0, 4.0], [5.0, 6.0, 7.0, 8.0]])
+    # q = 0: both logits are 0, so out = (v_0 + v_1) / (e^0 + 2) with v = the first two columns
+    o, lse = O.sparse_attention_row(np.zeros((1, 4)), kv, np.array([0.0]), 1.0, 2)
+    assert np.allclose(o, [[2.0, 8.0 / 3.0]], rtol=1e-15, atol=0)
+    assert np.isclose(lse[0], np.log(3.0), rtol=1e-15)
+    # q reads the last column only: logits 4 and 8 come from columns the value does not use
+    o, lse = O.sparse_attention_row(np.array([[0.0, 0.0, 0.0, 1.0]]), kv, np.array([0.0]), 1.0, 2)
+    z = 1.0 + np.exp(4.0) + np.exp(8.0)
+    assert np.allclose(o, [[(np.exp(4.0) * 1 + np.exp(8.0) * 5) / z, (np.exp(4.0) * 2 + np.exp(8.0) * 6) / z]],
+                       rtol=1e-14, atol=0)
+    assert np.isclose(lse[0], np.log(z), rtol=1e-15)
 
 
 def test_attention_is_stable_at_large_logits():
-    q, kv, sink, Dv = _rand_attn(24, n=30, scale=30.0)
-    o, lse = O.sparse_attention_row(q, kv, sink * 1000, 1.0, Dv)
-    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    """Logits far past exp's float64 range: adding c to every logit and to the sink leaves the
+    output unchanged and shifts lse by c; one logit 1000 above the rest returns its value row."""
+    g = np.random.default_rng(24)
+    v = g.standard_normal((6, 3))
+    l = g.standard_normal(6)
+    q = np.array([[0.0, 0.0, 0.0, 1.0]])
+    sink = np.array([0.3])
+    o, lse = O.sparse_attention_row(q, np.column_stack([v, l]), sink, 1.0, 3)
+    for c in (800.0, -800.0, 1e5):
+        o2, lse2 = O.sparse_attention_row(q, np.column_stack([v, l + c]), sink + c, 1.0, 3)
+        assert np.allclose(o2, o, rtol=1e-9, atol=1e-12) and np.isclose(lse2[0], lse[0] + c, rtol=1e-13)
+    l_dom = np.zeros(6)
+    l_dom[2] = 1000.0
+    o3, lse3 = O.sparse_attention_row(q, np.column_stack([v, l_dom]), np.array([0.0]), 1.0, 3)
+    assert np.array_equal(o3[0], v[2]) and lse3[0] == 1000.0
 
 
 @pytest.mark.parametrize("seed", [30, 31])
