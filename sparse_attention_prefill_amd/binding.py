@@ -83,6 +83,28 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _dense(name, t, dtype=None, optional=False, memory=True):
+    """A device tensor the library may read as dense row-major memory: on a GPU, contiguous and,
+    when given, of `dtype` (a torch dtype or a tuple of them). None is allowed when optional.
+    memory=False (host-only size queries, which read no tensor memory) checks the dtype only."""
+    if t is None:
+        if optional:
+            return
+        raise DsaError(f"{name} is required")
+    if memory and not t.is_cuda:
+        raise DsaError(f"{name} must be a GPU tensor")
+    if memory and not t.is_contiguous():
+        raise DsaError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise DsaError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _rows(name, t, dtype):
+    """Score rows: a GPU tensor whose rows are dense (stride(1) == 1); rows may be padded."""
+    if not t.is_cuda or t.dim() != 2 or t.dtype != dtype or t.stride(1) != 1:
+        raise DsaError(f"{name} must be a 2-D {dtype} GPU tensor with dense rows (stride(1) == 1)")
+
+
 def _stream(stream):
     s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
@@ -114,6 +136,9 @@ def build_cp_metadata(query_start_loc, seq_lens, num_tokens, cp_size, cp_rank, m
                       token_map=True, err_flag=None, stream=None):
     """Run the metadata kernel; returns a dict of int32 device tensors."""
     dev = query_start_loc.device
+    _dense("query_start_loc", query_start_loc, torch.int32)
+    _dense("seq_lens", seq_lens, torch.int32)
+    _dense("err_flag", err_flag, torch.int32, optional=True)
     B = seq_lens.numel()
     tpr, _, _ = cp_sizes(num_tokens, cp_size, cp_rank, mode, pad_to_cp)
     out = {
@@ -135,7 +160,20 @@ def build_cp_metadata(query_start_loc, seq_lens, num_tokens, cp_size, cp_rank, m
 
 def _indexer_args(q_idx, weights, k_idx, cu_seqlens_q, seqused_kv, cu_seqlens_kv, max_seqlen_kv, q_stride=1,
                   compress_ratio=1, topk=2048, kv_row_base=0, window=0, window_kv_start=None, q_scale=None,
-                  k_scale=None, topk_idx=None, workspace=None, err_flag=None):
+                  k_scale=None, topk_idx=None, workspace=None, err_flag=None, memory=True):
+    _dense("q_idx", q_idx, memory=memory)
+    _dense("k_idx", k_idx, q_idx.dtype, memory=memory)
+    _dense("weights", weights, torch.float32, memory=memory)
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("seqused_kv", seqused_kv), ("cu_seqlens_kv", cu_seqlens_kv)):
+        _dense(name, t, torch.int32, memory=memory)
+    _dense("window_kv_start", window_kv_start, torch.int32, optional=True, memory=memory)
+    _dense("q_scale", q_scale, torch.float32, optional=True, memory=memory)
+    _dense("k_scale", k_scale, torch.float32, optional=True, memory=memory)
+    _dense("topk_idx", topk_idx, torch.int32, optional=True, memory=memory)
+    _dense("workspace", workspace, optional=True, memory=memory)
+    _dense("err_flag", err_flag, torch.int32, optional=True, memory=memory)
+    if topk_idx is not None and tuple(topk_idx.shape) != (q_idx.shape[0], int(topk) + int(window)):
+        raise DsaError(f"topk_idx must be [{q_idx.shape[0]}, {int(topk) + int(window)}], got {tuple(topk_idx.shape)}")
     a = IndexerArgs()
     a.q_idx, a.q_scale, a.weights = _ptr(q_idx), _ptr(q_scale), _ptr(weights)
     a.k_idx, a.k_scale = _ptr(k_idx), _ptr(k_scale)
@@ -154,7 +192,9 @@ def _indexer_args(q_idx, weights, k_idx, cu_seqlens_q, seqused_kv, cu_seqlens_kv
 
 
 def indexer_topk_workspace(q_idx, weights, k_idx, cu_seqlens_q, seqused_kv, cu_seqlens_kv, max_seqlen_kv, **kw):
-    a = _indexer_args(q_idx, weights, k_idx, cu_seqlens_q, seqused_kv, cu_seqlens_kv, max_seqlen_kv, **kw)
+    """Workspace bytes of indexer_topk (host only: no tensor memory is read)."""
+    a = _indexer_args(q_idx, weights, k_idx, cu_seqlens_q, seqused_kv, cu_seqlens_kv, max_seqlen_kv, memory=False,
+                      **kw)
     n = lib().dsa_indexer_topk_workspace(ctypes.byref(a))
     if n == 0:
         raise DsaError(lib().dsa_last_error().decode())
@@ -179,6 +219,7 @@ def indexer_topk(q_idx, weights, k_idx, cu_seqlens_q, seqused_kv, cu_seqlens_kv,
 
 def indexer_scores(q_idx, weights, k_idx, cu_seqlens_q, seqused_kv, cu_seqlens_kv, max_seqlen_kv, scores,
                    stream=None, **kw):
+    _rows("scores", scores, torch.float32)
     a = _indexer_args(q_idx, weights, k_idx, cu_seqlens_q, seqused_kv, cu_seqlens_kv, max_seqlen_kv, **kw)
     _check(lib().dsa_indexer_scores(ctypes.byref(a), _ptr(scores), scores.stride(0), _stream(stream)),
            "dsa_indexer_scores")
@@ -191,6 +232,7 @@ def topk_from_scores(q_idx, weights, k_idx, cu_seqlens_q, seqused_kv, cu_seqlens
     window = kw.get("window", 0)
     if topk_idx is None:
         topk_idx = torch.empty(q_idx.shape[0], topk + window, dtype=torch.int32, device=scores.device)
+    _rows("scores", scores, torch.float32)
     a = _indexer_args(q_idx, weights, k_idx, cu_seqlens_q, seqused_kv, cu_seqlens_kv, max_seqlen_kv,
                       topk_idx=topk_idx, **kw)
     _check(lib().dsa_topk_from_scores(ctypes.byref(a), _ptr(scores), scores.stride(0), _stream(stream)),
@@ -203,6 +245,21 @@ def sparse_attn(q, kv, idx, sink, softmax_scale, d_v, out=None, lse=None, err_fl
     nq, H, Dqk = q.shape
     if out is None:
         out = torch.empty(nq, H, d_v, dtype=q.dtype, device=q.device)
+    _dense("q", q)
+    _dense("kv", kv, q.dtype)
+    _dense("idx", idx, torch.int32, optional=True)
+    _dense("sink", sink, torch.float32, optional=True)
+    _dense("out", out, q.dtype)
+    _dense("lse", lse, torch.float32, optional=True)
+    _dense("err_flag", err_flag, torch.int32, optional=True)
+    if tuple(out.shape) != (nq, H, d_v):
+        raise DsaError(f"out must be [{nq}, {H}, {d_v}], got {tuple(out.shape)}")
+    if idx is not None and (idx.dim() != 2 or idx.shape[0] != nq):
+        raise DsaError(f"idx must be [{nq}, k_tot], got {tuple(idx.shape)}")
+    if sink is not None and sink.numel() != H:
+        raise DsaError(f"sink must hold {H} values, got {sink.numel()}")
+    if lse is not None and tuple(lse.shape) != (nq, H):
+        raise DsaError(f"lse must be [{nq}, {H}], got {tuple(lse.shape)}")
     a = AttnArgs()
     a.q, a.kv, a.idx, a.sink, a.out, a.lse, a.err_flag = (_ptr(q), _ptr(kv), _ptr(idx), _ptr(sink), _ptr(out),
                                                           _ptr(lse), _ptr(err_flag))
@@ -220,6 +277,11 @@ def rerange(x, num_tokens, cp_size, mode, pad_to_cp, inverse=False, out=None, st
     n_out = rows_concat if inverse else num_tokens
     if out is None:
         out = torch.empty((n_out,) + tuple(x.shape[1:]), dtype=x.dtype, device=x.device)
+    _dense("x", x)
+    _dense("out", out, x.dtype)
+    n_in = num_tokens if inverse else rows_concat
+    if x.shape[0] < n_in or out.shape[0] < n_out or tuple(x.shape[1:]) != tuple(out.shape[1:]):
+        raise DsaError(f"rerange: x needs {n_in} rows and out {n_out} rows of the same shape")
     row_bytes = x[0].numel() * x.element_size() if x.shape[0] else out[0].numel() * out.element_size()
     _check(lib().dsa_rerange(_ptr(x), _ptr(out), num_tokens, row_bytes, cp_size, _mode(mode), int(pad_to_cp),
                              int(inverse), _stream(stream)), "dsa_rerange")

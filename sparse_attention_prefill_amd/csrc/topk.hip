@@ -180,15 +180,18 @@ struct RowInfo {
 template <int NT>
 __device__ inline bool row_setup(const int32_t* __restrict__ cu_q, const int32_t* __restrict__ used_kv,
                                  const int32_t* __restrict__ cu_kv, const int32_t* __restrict__ win_kv, int batch,
-                                 int stride, int ratio, int max_vis, int row_cap, int K, int window, int kv_row_base,
-                                 int32_t* orow, int32_t* err_flag, RowInfo* ri, int skip_above = INT32_MAX) {
+                                 int stride, int ratio, int nk, int max_vis, int row_cap, int K, int window,
+                                 int kv_row_base, int32_t* orow, int32_t* err_flag, RowInfo* ri,
+                                 int skip_above = INT32_MAX) {
   const int i = blockIdx.x, tid = threadIdx.x;
   const int k_tot = K + window;
   QueryView v;
   const bool have = query_view(cu_q, used_kv, cu_kv, batch, stride, i, &v);
   const int ev = have ? (ratio > 1 ? v.E / ratio : v.E) : 0;
-  if (have && v.E >= 1 && ev > skip_above && ev <= max_vis) return false;  // selected from a candidate list
-  if (!(have && v.E >= 1 && ev <= max_vis)) {
+  // the indexer's test of a usable row: a causal extent inside the key buffer
+  const bool ok = have && v.E >= 1 && ev <= max_vis && v.kv0 >= 0 && int64_t(v.kv0) + ev <= nk;
+  if (ok && ev > skip_above) return false;  // selected from a candidate list
+  if (!ok) {
     if (tid == 0) raise_flag(err_flag, DSA_DEVERR_EXTENT);
     for (int j = tid; j < k_tot; j += NT) orow[j] = -1;
     return false;
@@ -239,7 +242,7 @@ struct RegShared {
 template <int NT, int EPT>
 __global__ __launch_bounds__(NT, NT == 1024 ? 8 : 1) void topk_reg_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ used_kv,
-    const int32_t* __restrict__ cu_kv, const int32_t* __restrict__ win_kv, int batch, int stride, int ratio,
+    const int32_t* __restrict__ cu_kv, const int32_t* __restrict__ win_kv, int batch, int stride, int ratio, int nk,
     int max_vis, int K, int window, int kv_row_base, int32_t* __restrict__ out, int32_t* __restrict__ err_flag,
     int skip_above) {
   static_assert(EPT % 4 == 0 && EPT <= 64, "chunks come in groups of 4; one chunk per lane / thread");
@@ -251,8 +254,8 @@ __global__ __launch_bounds__(NT, NT == 1024 ? 8 : 1) void topk_reg_kernel(
   const int sel_wave = 0;  // runs the single-wave selects
   int32_t* orow = out + int64_t(blockIdx.x) * (K + window);
   RowInfo ri;
-  if (!row_setup<NT>(cu_q, used_kv, cu_kv, win_kv, batch, stride, ratio, max_vis, NT * EPT, K, window, kv_row_base,
-                     orow, err_flag, &ri, skip_above))
+  if (!row_setup<NT>(cu_q, used_kv, cu_kv, win_kv, batch, stride, ratio, nk, max_vis, NT * EPT, K, window,
+                     kv_row_base, orow, err_flag, &ri, skip_above))
     return;
   const int ev = ri.ev;
   const float* srow = scores + int64_t(blockIdx.x) * ld;
@@ -714,13 +717,13 @@ __device__ __attribute__((always_inline)) inline void stream_select(const float*
 
 __global__ __launch_bounds__(kStreamNT, 8) void topk_stream_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ used_kv,
-    const int32_t* __restrict__ cu_kv, const int32_t* __restrict__ win_kv, int batch, int stride, int ratio,
+    const int32_t* __restrict__ cu_kv, const int32_t* __restrict__ win_kv, int batch, int stride, int ratio, int nk,
     int max_vis, int K, int window, int kv_row_base, int32_t* __restrict__ out, int32_t* __restrict__ err_flag,
     int skip_above) {
   __shared__ StreamShared sh;
   int32_t* orow = out + int64_t(blockIdx.x) * (K + window);
   RowInfo ri;
-  if (!row_setup<kStreamNT>(cu_q, used_kv, cu_kv, win_kv, batch, stride, ratio, max_vis, kMaxRow, K, window,
+  if (!row_setup<kStreamNT>(cu_q, used_kv, cu_kv, win_kv, batch, stride, ratio, nk, max_vis, kMaxRow, K, window,
                             kv_row_base, orow, err_flag, &ri, skip_above))
     return;
   stream_select(scores + int64_t(blockIdx.x) * ld, ld, ri.ev, K, ri.base, orow, sh);
@@ -912,7 +915,7 @@ struct CandShared {
 __global__ __launch_bounds__(kCandNT, 2) void topk_cand_kernel(
     const uint2* __restrict__ cand, const int32_t* __restrict__ n_cand, int32_t* __restrict__ status,
     const uint32_t* __restrict__ theta, int cap, int segs, int fuse_above, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ used_kv,
-    const int32_t* __restrict__ cu_kv, const int32_t* __restrict__ win_kv, int batch, int stride, int ratio,
+    const int32_t* __restrict__ cu_kv, const int32_t* __restrict__ win_kv, int batch, int stride, int ratio, int nk,
     int max_vis, int K, int window, int kv_row_base, int32_t* __restrict__ out, int32_t* __restrict__ err_flag) {
   constexpr int NT = kCandNT, NW = NT / 64;
   __shared__ CandShared sh;
@@ -921,11 +924,12 @@ __global__ __launch_bounds__(kCandNT, 2) void topk_cand_kernel(
   QueryView v;
   const bool have = query_view(cu_q, used_kv, cu_kv, batch, stride, row, &v);
   const int ev = have ? (ratio > 1 ? v.E / ratio : v.E) : 0;
-  if (!have || v.E < 1 || ev <= fuse_above || ev > max_vis) return;  // not a candidate row
+  // not a candidate row (rows outside the key buffer are flagged and cleared by topk_reg_kernel)
+  if (!have || v.E < 1 || ev <= fuse_above || ev > max_vis || v.kv0 < 0 || int64_t(v.kv0) + ev > nk) return;
   int32_t* orow = out + int64_t(row) * (K + window);
   RowInfo ri;
-  if (!row_setup<NT>(cu_q, used_kv, cu_kv, win_kv, batch, stride, ratio, max_vis, kMaxRow, K, window, kv_row_base,
-                     orow, err_flag, &ri))
+  if (!row_setup<NT>(cu_q, used_kv, cu_kv, win_kv, batch, stride, ratio, nk, max_vis, kMaxRow, K, window,
+                     kv_row_base, orow, err_flag, &ri))
     return;
   // the list: segment y holds its first min(count_y, seg_cap) slots; a segment that overflowed
   // or a list shorter than K sends the row to the recompute
@@ -1064,7 +1068,7 @@ dsa_status launch_topk(const dsa_indexer_topk_args* a, const float* scores, int6
   const dim3 grid(a->nq);
 #define DSA_TOPK_ARGS                                                                                          \
   scores, ld, a->cu_seqlens_q, a->seqused_kv, a->cu_seqlens_kv, a->window_kv_start, a->batch, a->q_stride,     \
-      a->compress_ratio, max_vis, a->topk, a->window, a->kv_row_base, a->topk_idx, a->err_flag, INT32_MAX
+      a->compress_ratio, a->nk, max_vis, a->topk, a->window, a->kv_row_base, a->topk_idx, a->err_flag, INT32_MAX
 #define DSA_TOPK_REG(NT, E) hipLaunchKernelGGL((topk_reg_kernel<NT, E>), grid, dim3(NT), 0, stream, DSA_TOPK_ARGS)
   if (max_vis <= 256 * 16) DSA_TOPK_REG(256, 16);
   else if (max_vis <= 512 * 16) DSA_TOPK_REG(512, 16);
@@ -1100,13 +1104,13 @@ dsa_status launch_topk_candidates(const dsa_indexer_topk_args* a, const float* s
   const dim3 grid(a->nq);
   hipLaunchKernelGGL((topk_reg_kernel<1024, 32>), grid, dim3(1024), 0, stream, score_rows, ld, a->cu_seqlens_q,
                      a->seqused_kv, a->cu_seqlens_kv, a->window_kv_start, a->batch, a->q_stride, a->compress_ratio,
-                     max_vis, a->topk, a->window, a->kv_row_base, a->topk_idx, a->err_flag, cm.fuse_above);
+                     a->nk, max_vis, a->topk, a->window, a->kv_row_base, a->topk_idx, a->err_flag, cm.fuse_above);
   dsa_status st = check_launch("topk_reg_kernel");
   if (st != DSA_OK) return st;
   hipLaunchKernelGGL(topk_cand_kernel, grid, dim3(kCandNT), 0, stream, cm.cand, cm.n_cand, cm.status, cm.theta,
                      cm.cap, cm.segs, cm.fuse_above,
                      a->cu_seqlens_q, a->seqused_kv, a->cu_seqlens_kv, a->window_kv_start, a->batch, a->q_stride,
-                     a->compress_ratio, max_vis, a->topk, a->window, a->kv_row_base, a->topk_idx, a->err_flag);
+                     a->compress_ratio, a->nk, max_vis, a->topk, a->window, a->kv_row_base, a->topk_idx, a->err_flag);
   st = check_launch("topk_cand_kernel");
   if (st != DSA_OK) return st;
 #define DSA_REFILL_ARGS                                                                                       \

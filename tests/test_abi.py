@@ -102,3 +102,28 @@ def test_indexer_workspace_sizes_follow_the_selection_mode():
     assert D.indexer_topk_workspace(qi, w, ki, cu_q, used, cu_kv, 100000, topk=100000) == nq * 100032 * 4
     qs = torch.zeros(nq, 32, 128, dtype=torch.bfloat16)
     assert D.indexer_topk_workspace(qs, w[:, :32], ki, cu_q, used, cu_kv, 100000, topk=2048) == nq * 100032 * 4
+
+
+def test_binding_rejects_tensors_the_library_cannot_read():
+    """Marshalling checks: host tensors, non-contiguous views, mixed dtypes, padded score columns."""
+    import torch
+    import sparse_attention_prefill_amd as D
+    nq = 4
+    qi = torch.zeros(nq, 64, 128, dtype=torch.bfloat16)
+    w = torch.zeros(nq, 64)
+    cu = torch.tensor([0, nq], dtype=torch.int32)
+    used = torch.tensor([16], dtype=torch.int32)
+    with pytest.raises(D.DsaError, match="GPU"):
+        D.indexer_topk(qi, w, torch.zeros(16, 128, dtype=torch.bfloat16), cu, used, cu, 16, topk=8)
+    with pytest.raises(D.DsaError, match="dtype"):
+        D.indexer_topk_workspace(qi, w, torch.zeros(16, 128, dtype=torch.float32), cu, used, cu, 16, topk=8)
+    with pytest.raises(D.DsaError, match="dtype"):
+        D.indexer_topk_workspace(qi, w.double(), torch.zeros(16, 128, dtype=torch.bfloat16), cu, used, cu, 16)
+    with pytest.raises(D.DsaError, match="dense rows"):
+        D.indexer_scores(qi, w, qi[0], cu, used, cu, 16, torch.zeros(16, nq).t())
+    q = torch.zeros(2, 128, 576, dtype=torch.bfloat16)
+    with pytest.raises(D.DsaError, match="GPU"):
+        D.sparse_attn(q, torch.zeros(8, 576, dtype=torch.bfloat16), torch.zeros(2, 4, dtype=torch.int32),
+                      None, 0.1, 512)
+    with pytest.raises(D.DsaError, match="GPU|contiguous"):
+        D.rerange(torch.zeros(8, 64, dtype=torch.bfloat16)[:, ::2], 8, 2, 1, False)

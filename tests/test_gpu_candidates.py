@@ -86,3 +86,48 @@ def test_recomputed_rows_match_score_rows(name, kw, zero):
     dev = gpu()
     fused, ref, _ = _both(S.WORKLOADS[name].with_(**kw), "normal", dev, zero_keys=zero)
     assert np.array_equal(fused, ref)
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("inseq_cp8_last_8k", {"lens": (9000,), "topk": 512}),     # score rows
+    ("inseq_cp8_last_8k", {"lens": (100000,)}),                 # candidate lists
+    ("rr_cp4_r1_var8_cmp4", {"lens": (6000, 9000)}),            # x4 keys, window
+])
+def test_rows_outside_the_key_buffer_are_cleared_and_flagged(name, kw):
+    """A key buffer shorter than some rows' extents: those rows get -1 everywhere (window included)
+    and DSA_DEVERR_EXTENT; the other rows are exactly those of the full buffer."""
+    dev = gpu()
+    import sparse_attention_prefill_amd as D
+    wl = S.WORKLOADS[name].with_(**kw)
+    m = O.cp_metadata(wl.qsl, wl.seq_lens, wl.cp, wl.rank, wl.mode, wl.pad)
+    toks = m["token_map"][m["token_map"] >= 0]
+    inp = S.stream_inputs(wl)
+    qin = S.query_inputs(wl, toks, indexer_only=True)
+    ik = wl.idx_dtype
+    cu_kv = inp["kv_cmp_start"] if wl.compress > 1 else m["local_kv_start_loc"]
+    max_kv = int(m["local_seq_lens"].max())
+    k_full = inp["k_idx"]
+    nk_short = k_full.shape[0] - 37
+    views = O.query_views(m)
+    vis = [E // wl.compress if wl.compress > 1 else E for (_, E, _) in views]
+    kv0 = [int(cu_kv[b]) for (b, _, _) in views]
+    bad = np.array([k0 + e > nk_short for k0, e in zip(kv0, vis)])
+    assert bad.any() and not bad.all()
+    lkv = to_dev(m["local_kv_start_loc"], "i32", dev)
+    outs, errs = [], []
+    for k_idx in (k_full, k_full[:nk_short]):
+        err = torch.zeros(1, dtype=torch.int32, device=dev)
+        out = torch.full((len(toks), wl.k_tot), 777, dtype=torch.int32, device=dev)
+        print(f"case {name} nk={k_idx.shape[0]} nq={len(toks)}", flush=True)
+        D.indexer_topk(to_dev(qin["q_idx"], ik, dev), to_dev(qin["w"], "f32", dev), to_dev(k_idx, ik, dev),
+                       to_dev(m["local_query_start_loc"], "i32", dev), to_dev(m["local_seq_lens"], "i32", dev),
+                       to_dev(cu_kv, "i32", dev), max_kv, topk_idx=out, topk=wl.topk, q_stride=m["stride"],
+                       compress_ratio=wl.compress, kv_row_base=wl.n_kv if wl.compress > 1 else 0,
+                       window=wl.window, window_kv_start=lkv if wl.window else None, err_flag=err)
+        torch.cuda.synchronize()
+        outs.append(out.cpu().numpy())
+        errs.append(err.item())
+    assert errs[0] == 0 and errs[1] & 0x20
+    assert np.all(outs[1][bad] == -1)
+    assert np.array_equal(outs[1][~bad], outs[0][~bad])
+    assert not np.any(outs[0] == 777)

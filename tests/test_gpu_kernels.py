@@ -30,7 +30,8 @@ def _run_topk(scores, m, d, K, dev, ratio=1, window=0, win_start=None, kv_row_ba
     dummy_q = torch.zeros(nq, 1, 8, dtype=torch.float32, device=dev)
     dummy_k = torch.zeros(1, 8, dtype=torch.float32, device=dev)
     err = torch.zeros(1, dtype=torch.int32, device=dev)
-    out = D.topk_from_scores(dummy_q, dummy_q[:, :, 0], dummy_k, d["local_query_start_loc"], d["local_seq_lens"],
+    dummy_w = torch.zeros(nq, 1, dtype=torch.float32, device=dev)
+    out = D.topk_from_scores(dummy_q, dummy_w, dummy_k, d["local_query_start_loc"], d["local_seq_lens"],
                              d["local_kv_start_loc"], max_kv, to_dev(scores, "f32", dev), topk=K,
                              q_stride=m["stride"], compress_ratio=ratio, window=window,
                              window_kv_start=win_start, kv_row_base=kv_row_base, err_flag=err)
