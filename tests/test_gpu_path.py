@@ -2,8 +2,10 @@
 
 Each workload runs through the C ABI in the order and launch configuration the benchmark uses.
 The oracle checks: metadata bit-exact; top-k sets bit-exact on integer-valued inputs and within
-the tie band on Gaussian inputs; attention within tolerance on every row whose set matches.
-Full-size workloads are checked on sampled rows; reduced ones on every row.
+the tie band on Gaussian inputs; attention within tolerance on every checked row: end to end where
+the sets match, and on the oracle's own set (the attention entry point alone) where they differ.
+Full-size workloads are checked on at least 256 sampled rows, the first and last included;
+reduced ones on every row or 200 evenly spread rows.
 """
 import numpy as np
 import pytest
@@ -11,7 +13,7 @@ import torch
 
 import oracle as O
 import synthetic as S
-from dsa_testlib import gpu, to_dev, to_f64, assert_attn_close, check_topk_rows
+from dsa_testlib import gpu, to_dev, to_f64, assert_attn_close, check_topk_rows, SCORE_TOL, TIE_BAND
 
 pytestmark = pytest.mark.gpu
 
@@ -41,24 +43,32 @@ def gpu_rank_path(wl, variant, dev, rank=None, keep_scores=False):
               k_scale=to_dev(inp["k_scale"], "f32", dev) if "k_scale" in inp else None, err_flag=err)
     w_d = to_dev(qin["w"], "f32", dev)
     k_d = to_dev(inp["k_idx"], ik, dev)
+    print(f"case {wl.name} {variant} lens={wl.lens[:4]} cp={wl.cp} r={rank} K={wl.topk} nq={n_real}", flush=True)
     nbytes = D.indexer_topk_workspace(q_idx, w_d, k_d, meta["local_query_start_loc"], meta["local_seq_lens"], cu_kv,
                                       max_kv, **kw)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     idx = D.indexer_topk(q_idx, w_d, k_d, meta["local_query_start_loc"], meta["local_seq_lens"], cu_kv, max_kv,
                          workspace=ws, **kw)
-    out = D.sparse_attn(to_dev(qin["q"], wl.attn_dtype, dev), to_dev(inp["kv"], wl.attn_dtype, dev), idx,
-                        to_dev(inp["sink"], "f32", dev), 1.0 / np.sqrt(wl.Dqk), wl.Dv, err_flag=err)
+    q_d, kv_d, sink_d = to_dev(qin["q"], wl.attn_dtype, dev), to_dev(inp["kv"], wl.attn_dtype, dev), \
+        to_dev(inp["sink"], "f32", dev)
+    out = D.sparse_attn(q_d, kv_d, idx, sink_d, 1.0 / np.sqrt(wl.Dqk), wl.Dv, err_flag=err)
     torch.cuda.synchronize()
     res = dict(meta={k: (v.cpu().numpy() if v is not None else None) for k, v in meta.items()}, err=err.item(),
-               idx=idx.cpu().numpy(), out=out, toks=toks, inp=inp, qin=qin, n_real=n_real, tpr=tpr)
+               idx=idx.cpu().numpy(), out=out, toks=toks, inp=inp, qin=qin, n_real=n_real, tpr=tpr,
+               q_d=q_d, kv_d=kv_d, sink_d=sink_d)
     if keep_scores:  # full score rows from the two-stage entry point (the fused call may keep none)
         vis = max_kv // wl.compress if wl.compress > 1 else max_kv
         sc = torch.empty(max(n_real, 1), (vis + 63) // 64 * 64, dtype=torch.float32, device=dev)
         D.indexer_scores(q_idx, w_d, k_d, meta["local_query_start_loc"], meta["local_seq_lens"], cu_kv, max_kv, sc,
                          **{k: v for k, v in kw.items() if k not in ("window", "window_kv_start", "kv_row_base")})
         torch.cuda.synchronize()
-        res["scores"] = sc[:n_real].cpu().numpy()
+        res["scores_dev"] = sc
     return res
+
+
+def sampled_rows(n, count):
+    """count evenly spread rows of n, always with the first two and the last two."""
+    return np.unique(np.concatenate([[0, 1, n - 2, n - 1], np.linspace(0, n - 1, count).astype(int)]))
 
 
 def check_against_oracle(wl, variant, res, rows=None, min_same=0.99):
@@ -80,7 +90,7 @@ def check_against_oracle(wl, variant, res, rows=None, min_same=0.99):
         same = len(rows)
     else:
         same = check_topk_rows(gpu_topk, ora["topk_ids"], ora["scores"], K, base, rows=rows,
-                               delta_rel=1e-4 if wl.idx_dtype == "fp8" else 1e-5)
+                               delta_rel=TIE_BAND[wl.idx_dtype])
     assert same >= min_same * len(rows), f"only {same}/{len(rows)} rows with identical sets"
     if wl.window:
         for n_, i in enumerate(rows):
@@ -90,6 +100,22 @@ def check_against_oracle(wl, variant, res, rows=None, min_same=0.99):
     keep = [n_ for n_, i in enumerate(rows)
             if np.array_equal(np.sort(gpu_topk[n_][gpu_topk[n_] >= 0]), ora["topk_ids"][n_])]
     assert_attn_close(got[[rows[k] for k in keep]], ora["out"][keep], wl.attn_dtype, wl.name)
+    # rows whose sets differ (near-ties at the cut): the attention entry point alone on the oracle's set
+    diff = [n_ for n_ in range(len(rows)) if n_ not in set(keep)]
+    if diff:
+        import sparse_attention_prefill_amd as D
+        dev = res["q_d"].device
+        idx_o = np.full((len(diff), wl.k_tot), -1, dtype=np.int32)
+        for j, n_ in enumerate(diff):
+            sel = np.concatenate([ora["topk_ids"][n_], ora["window_ids"][n_]])
+            idx_o[j, :len(sel)] = sel
+        q_rows = res["q_d"][torch.as_tensor([rows[n_] for n_ in diff], device=dev)].contiguous()
+        o_iso = D.sparse_attn(q_rows, res["kv_d"], to_dev(idx_o, "i32", dev), res["sink_d"], 1.0 / np.sqrt(wl.Dqk),
+                              wl.Dv)
+        torch.cuda.synchronize()
+        assert_attn_close(to_f64(o_iso), ora["out"][diff], wl.attn_dtype, f"{wl.name} (oracle's sets)")
+    print(f"checked {len(rows)} rows: {same} identical top-k sets, {len(diff)} attended on the oracle's set",
+          flush=True)
     return ora
 
 
@@ -133,9 +159,7 @@ def test_path_full_size_integer_inputs_sampled(name):
     dev = gpu()
     wl = S.WORKLOADS[name]
     res = gpu_rank_path(wl, "int", dev)
-    n = res["n_real"]
-    rows = np.unique(np.concatenate([[0, 1, n - 2, n - 1], np.linspace(0, n - 1, 8).astype(int)]))
-    check_against_oracle(wl, "int", res, rows=rows)
+    check_against_oracle(wl, "int", res, rows=sampled_rows(res["n_real"], 256))
 
 
 @pytest.mark.parametrize("name", ["inseq_cp8_last_8k", "rr_cp8_r3_batch4", "rr_cp4_r1_var8_cmp4", "long_131k_fp8",
@@ -144,15 +168,18 @@ def test_path_full_size_sampled(name):
     dev = gpu()
     wl = S.WORKLOADS[name]
     res = gpu_rank_path(wl, "normal", dev, keep_scores=True)
-    n = res["n_real"]
-    rows = np.unique(np.concatenate([[0, 1, n - 2, n - 1], np.linspace(0, n - 1, 10).astype(int)]))
-    ora = check_against_oracle(wl, "normal", res, rows=rows, min_same=0.75)
+    rows = sampled_rows(res["n_real"], 256)
+    ora = check_against_oracle(wl, "normal", res, rows=rows, min_same=0.9)
+    got = res.pop("scores_dev")[torch.as_tensor(rows, device=res["q_d"].device)].cpu().numpy()
+    worst = 0.0
     for n_, i in enumerate(rows):  # the score rows themselves (rows the top-k keeps whole have none)
         ref = ora["scores"][n_]
-        g = res["scores"][i, :len(ref)].astype(np.float64)
+        g = got[n_, :len(ref)].astype(np.float64)
         if len(ref) > wl.topk:
-            tol = (1e-4 if wl.idx_dtype == "fp8" else 2e-5) * max(np.abs(ref).max(), 1e-30)
-            assert np.abs(g - ref).max() <= tol, (name, i)
+            dev_rel = np.abs(g - ref).max() / max(np.abs(ref).max(), 1e-30)
+            worst = max(worst, dev_rel)
+            assert dev_rel <= SCORE_TOL[wl.idx_dtype], (name, i, dev_rel)
+    print(f"worst score deviation / max|score|: {worst:.3e}", flush=True)
 
 
 @pytest.mark.parametrize("name,kw", [("rr_cp8_r3_batch4", {"lens": (2100, 900, 300, 5), "topk": 256}),
