@@ -182,6 +182,25 @@ dsa_status dsa_indexer_scores(const dsa_indexer_topk_args* args, float* scores, 
 dsa_status dsa_topk_from_scores(const dsa_indexer_topk_args* args, const float* scores,
                                 int64_t ld, void* stream);
 
+/* Measurement hook, for benchmarks and profilers that time the kernels inside one call:
+ * dsa_indexer_topk(args, stream), with events[k] recorded on `stream` right before the k-th
+ * kernel the call launches and events[n] right after the last one, n = *n_kernels (out), so
+ * hipEventElapsedTime(events[k], events[k+1]) is the k-th kernel's time. events are hipEvent_t
+ * handles created by the caller (with timing enabled to read durations); kernels past the
+ * (n_events - 1)-th run unbracketed. kernel_names (optional, n_events entries) receives static
+ * strings naming the kernels. Errors: those of dsa_indexer_topk; DSA_ERR_INVALID_ARG for fewer
+ * than 2 events or a NULL event; DSA_ERR_HIP if an event cannot be recorded. */
+dsa_status dsa_indexer_topk_timed(const dsa_indexer_topk_args* args, void* stream, void* const* events,
+                                  int32_t n_events, int32_t* n_kernels, const char** kernel_names);
+
+/* Measurement hook, for benchmarks that report the graphics clock a run held: enqueues on
+ * `stream` one wave that reads the shader-clock counter and the 100 MHz real-time counter, spins
+ * for `ticks` real-time ticks (1 .. 1e7, i.e. 10 ns .. 100 ms) and reads both again, writing
+ * {clock0, clock1, realtime0, realtime1} to out (device, 4 x uint64). The clock in MHz is
+ * 100 * (clock1 - clock0) / (realtime1 - realtime0). DSA_ERR_INVALID_ARG for a NULL out or ticks
+ * out of range. */
+dsa_status dsa_clock_probe(uint64_t* out, int64_t ticks, void* stream);
+
 /* ------------------------------------------------------------------------------------------
  * (4) Sparse shared-KV (MLA) attention with a per-head sink ([xLLM-CP] Design, data-flow
  * step (4): the local queries of all heads attend over the full KV stream's selected rows and

@@ -59,12 +59,16 @@ def lib():
         L.dsa_indexer_topk_workspace.argtypes = [ctypes.POINTER(IndexerArgs)]
         L.dsa_indexer_topk_workspace.restype = c_size
         L.dsa_indexer_topk.argtypes = [ctypes.POINTER(IndexerArgs), c_p]
+        L.dsa_indexer_topk_timed.argtypes = [ctypes.POINTER(IndexerArgs), c_p, ctypes.POINTER(c_p), c_i32,
+                                             ctypes.POINTER(c_i32), ctypes.POINTER(ctypes.c_char_p)]
         L.dsa_indexer_scores.argtypes = [ctypes.POINTER(IndexerArgs), c_p, c_i64, c_p]
         L.dsa_topk_from_scores.argtypes = [ctypes.POINTER(IndexerArgs), c_p, c_i64, c_p]
         L.dsa_sparse_attn.argtypes = [ctypes.POINTER(AttnArgs), c_p]
+        L.dsa_clock_probe.argtypes = [c_p, c_i64, c_p]
         L.dsa_rerange.argtypes = [c_p, c_p, c_i32, c_i64, c_i32, c_i32, c_i32, c_i32, c_p]
-        for f in ("dsa_cp_sizes", "dsa_build_cp_metadata", "dsa_indexer_topk", "dsa_indexer_scores",
-                  "dsa_topk_from_scores", "dsa_sparse_attn", "dsa_rerange"):
+        for f in ("dsa_cp_sizes", "dsa_build_cp_metadata", "dsa_indexer_topk", "dsa_indexer_topk_timed",
+                  "dsa_indexer_scores",
+                  "dsa_topk_from_scores", "dsa_sparse_attn", "dsa_rerange", "dsa_clock_probe"):
             getattr(L, f).restype = c_i32
         _lib = L
     return _lib
@@ -217,6 +221,24 @@ def indexer_topk(q_idx, weights, k_idx, cu_seqlens_q, seqused_kv, cu_seqlens_kv,
     return topk_idx
 
 
+def indexer_topk_timed(q_idx, weights, k_idx, cu_seqlens_q, seqused_kv, cu_seqlens_kv, max_seqlen_kv, events,
+                       topk_idx, workspace, stream=None, **kw):
+    """indexer_topk with events[k] recorded right before the k-th kernel it launches and events[n]
+    right after the last; returns the n kernel names. events: torch.cuda.Event(enable_timing=True)
+    objects that have been recorded once already (torch creates the HIP event on first record)."""
+    handles = [int(e.cuda_event) for e in events]
+    if len(handles) < 2 or not all(handles):
+        raise DsaError("indexer_topk_timed: need at least 2 events, each recorded once before")
+    arr = (c_p * len(handles))(*handles)
+    names = (ctypes.c_char_p * len(handles))()
+    n = c_i32(0)
+    a = _indexer_args(q_idx, weights, k_idx, cu_seqlens_q, seqused_kv, cu_seqlens_kv, max_seqlen_kv,
+                      topk_idx=topk_idx, workspace=workspace, **kw)
+    _check(lib().dsa_indexer_topk_timed(ctypes.byref(a), _stream(stream), arr, len(handles), ctypes.byref(n), names),
+           "dsa_indexer_topk_timed")
+    return [names[k].decode() for k in range(n.value)]
+
+
 def indexer_scores(q_idx, weights, k_idx, cu_seqlens_q, seqused_kv, cu_seqlens_kv, max_seqlen_kv, scores,
                    stream=None, **kw):
     _rows("scores", scores, torch.float32)
@@ -238,6 +260,22 @@ def topk_from_scores(q_idx, weights, k_idx, cu_seqlens_q, seqused_kv, cu_seqlens
     _check(lib().dsa_topk_from_scores(ctypes.byref(a), _ptr(scores), scores.stride(0), _stream(stream)),
            "dsa_topk_from_scores")
     return topk_idx
+
+
+def clock_probe(out, ticks=20000, stream=None):
+    """Enqueue the clock probe: out (uint64 or int64 GPU tensor of 4) receives the shader-clock and
+    100 MHz real-time counters before and after a spin of `ticks` real-time ticks."""
+    _dense("out", out, (torch.int64,))
+    if out.numel() < 4:
+        raise DsaError("clock_probe: out needs 4 entries")
+    _check(lib().dsa_clock_probe(_ptr(out), int(ticks), _stream(stream)), "dsa_clock_probe")
+    return out
+
+
+def probe_mhz(out):
+    """The shader clock in MHz from a clock_probe result (host copy of its 4 counters)."""
+    c0, c1, r0, r1 = (int(x) for x in out[:4])
+    return 100.0 * (c1 - c0) / max(r1 - r0, 1)
 
 
 def sparse_attn(q, kv, idx, sink, softmax_scale, d_v, out=None, lse=None, err_flag=None, stream=None):

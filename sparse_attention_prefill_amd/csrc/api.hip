@@ -2,7 +2,6 @@
 #include <string.h>
 
 #include <algorithm>
-
 #include <string>
 
 #include "dsa_internal.h"
@@ -10,6 +9,25 @@
 namespace dsa {
 
 static thread_local std::string g_last_error;
+
+// The events of the calling thread's dsa_indexer_topk_timed call, if one is running.
+struct LaunchTap {
+  void* const* events;
+  int cap;                 // events available
+  int n;                   // events recorded
+  const char** names;      // optional: names[k] = kernel launched after events[k]
+  hipError_t err;          // first failed record
+};
+static thread_local LaunchTap* g_tap = nullptr;
+
+void tap_launch(const char* kernel, hipStream_t stream) {
+  LaunchTap* t = g_tap;
+  if (!t || t->n >= t->cap - 1) return;  // the last event is kept for the end of the call
+  const hipError_t e = hipEventRecord(static_cast<hipEvent_t>(t->events[t->n]), stream);
+  if (e != hipSuccess && t->err == hipSuccess) t->err = e;
+  if (t->names) t->names[t->n] = kernel;
+  ++t->n;
+}
 
 void set_error(const std::string& msg) { g_last_error = msg; }
 void clear_error() { g_last_error.clear(); }
@@ -78,6 +96,22 @@ CandLayout cand_layout(const dsa_indexer_topk_args* a) {
   return L;
 }
 
+// One wave reads the shader-clock counter (s_memtime) and the 100 MHz real-time counter, spins
+// until `ticks` real-time ticks have passed, and reads both again: out = {c0, c1, r0, r1}.
+__global__ void clock_probe_kernel(uint64_t* __restrict__ out, uint64_t ticks) {
+  const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+  const uint64_t c0 = __builtin_amdgcn_s_memtime();
+  uint64_t r = r0;
+  while (r - r0 < ticks) r = __builtin_amdgcn_s_memrealtime();
+  const uint64_t c1 = __builtin_amdgcn_s_memtime();
+  if (threadIdx.x == 0) {
+    out[0] = c0;
+    out[1] = c1;
+    out[2] = r0;
+    out[3] = r;
+  }
+}
+
 dsa_status check_indexer_args(const dsa_indexer_topk_args* a, bool need_out) {
   if (!a) return fail(DSA_ERR_INVALID_ARG, "indexer: args is NULL");
   if (a->nq < 0 || a->nk < 0 || a->batch < 0 || a->n_heads < 1 || a->head_dim < 1)
@@ -104,6 +138,39 @@ dsa_status check_indexer_args(const dsa_indexer_topk_args* a, bool need_out) {
   const bool mfma = a->n_heads == 64 && a->head_dim == 128;
   if (a->dtype == DSA_FP8_E4M3 && !mfma) return fail(DSA_ERR_UNSUPPORTED, "indexer: fp8 needs 64 heads x 128");
   return DSA_OK;
+}
+
+size_t workspace_need(const dsa_indexer_topk_args* a) {
+  return candidate_mode(a) ? cand_layout(a).total : size_t(a->nq) * size_t(score_ld(a)) * sizeof(float);
+}
+
+// Indexer + top-k of checked arguments with a large enough workspace, on stream s.
+dsa_status run_indexer_topk(const dsa_indexer_topk_args* a, hipStream_t s) {
+  dsa_status st;
+  if (!candidate_mode(a)) {
+    float* scores = static_cast<float*>(a->workspace);
+    // rows with at most topk visible keys are taken whole by the top-k: the indexer skips them
+    st = launch_indexer_scores(a, scores, score_ld(a), max_visible(a), a->topk, nullptr, s);
+    if (st != DSA_OK) return st;
+    return launch_topk(a, scores, score_ld(a), max_visible(a), s);
+  }
+  const CandLayout L = cand_layout(a);
+  char* ws = static_cast<char*>(a->workspace);
+  CandidateMode cm;
+  cm.fuse_above = std::max(kFuseMin, a->topk);
+  cm.theta = reinterpret_cast<uint32_t*>(ws + L.theta);
+  cm.n_cand = reinterpret_cast<int32_t*>(ws + L.n_cand);
+  cm.status = reinterpret_cast<int32_t*>(ws + L.status);
+  cm.cand = reinterpret_cast<uint2*>(ws + L.slots);
+  cm.cap = kFuseCap;
+  cm.segs = L.segs;
+  float* score_rows = reinterpret_cast<float*>(ws + L.slots);  // short rows: kFuseMin floats per slot
+  st = launch_topk_theta(a, max_visible(a), cm, s);
+  if (st != DSA_OK) return st;
+  st = launch_indexer_scores(a, score_rows, kFuseMin, max_visible(a), a->topk, &cm, s);
+  if (st != DSA_OK) return st;
+  return launch_topk_candidates(a, score_rows, kFuseMin, max_visible(a), cm, reinterpret_cast<float*>(ws + L.scratch),
+                                L.sld, L.n_scratch, s);
 }
 
 }  // namespace
@@ -183,36 +250,38 @@ dsa_status dsa_indexer_topk(const dsa_indexer_topk_args* a, void* stream) {
   dsa_status st = check_indexer_args(a, true);
   if (st != DSA_OK) return st;
   if (a->nq == 0) return DSA_OK;
-  const bool cmode = candidate_mode(a);
-  const size_t need = cmode ? cand_layout(a).total : size_t(a->nq) * size_t(score_ld(a)) * sizeof(float);
-  if (!a->workspace || a->workspace_bytes < need || (reinterpret_cast<uintptr_t>(a->workspace) & 255u))
+  if (!a->workspace || a->workspace_bytes < workspace_need(a) || (reinterpret_cast<uintptr_t>(a->workspace) & 255u))
     return fail(DSA_ERR_WORKSPACE, "indexer_topk: workspace missing, not 256-byte aligned or smaller than "
                                        "dsa_indexer_topk_workspace()");
-  hipStream_t s = as_stream(stream);
-  if (!cmode) {
-    float* scores = static_cast<float*>(a->workspace);
-    // rows with at most topk visible keys are taken whole by the top-k: the indexer skips them
-    st = launch_indexer_scores(a, scores, score_ld(a), max_visible(a), a->topk, nullptr, s);
-    if (st != DSA_OK) return st;
-    return launch_topk(a, scores, score_ld(a), max_visible(a), s);
+  return run_indexer_topk(a, as_stream(stream));
+}
+
+dsa_status dsa_indexer_topk_timed(const dsa_indexer_topk_args* a, void* stream, void* const* events,
+                                  int32_t n_events, int32_t* n_kernels, const char** kernel_names) {
+  clear_error();
+  if (!events || n_events < 2) return fail(DSA_ERR_INVALID_ARG, "indexer_topk_timed: need at least 2 events");
+  for (int k = 0; k < n_events; ++k)
+    if (!events[k]) return fail(DSA_ERR_INVALID_ARG, "indexer_topk_timed: NULL event");
+  LaunchTap tap{events, n_events, 0, kernel_names, hipSuccess};
+  g_tap = &tap;
+  dsa_status st = dsa_indexer_topk(a, stream);
+  g_tap = nullptr;
+  if (st != DSA_OK) return st;
+  if (tap.n > 0) {
+    const hipError_t e = hipEventRecord(static_cast<hipEvent_t>(events[tap.n]), as_stream(stream));
+    if (e != hipSuccess && tap.err == hipSuccess) tap.err = e;
   }
-  const CandLayout L = cand_layout(a);
-  char* ws = static_cast<char*>(a->workspace);
-  CandidateMode cm;
-  cm.fuse_above = std::max(kFuseMin, a->topk);
-  cm.theta = reinterpret_cast<uint32_t*>(ws + L.theta);
-  cm.n_cand = reinterpret_cast<int32_t*>(ws + L.n_cand);
-  cm.status = reinterpret_cast<int32_t*>(ws + L.status);
-  cm.cand = reinterpret_cast<uint2*>(ws + L.slots);
-  cm.cap = kFuseCap;
-  cm.segs = L.segs;
-  float* score_rows = reinterpret_cast<float*>(ws + L.slots);  // short rows: kFuseMin floats per slot
-  st = launch_topk_theta(a, max_visible(a), cm, s);
-  if (st != DSA_OK) return st;
-  st = launch_indexer_scores(a, score_rows, kFuseMin, max_visible(a), a->topk, &cm, s);
-  if (st != DSA_OK) return st;
-  return launch_topk_candidates(a, score_rows, kFuseMin, max_visible(a), cm, reinterpret_cast<float*>(ws + L.scratch),
-                                L.sld, L.n_scratch, s);
+  if (tap.err != hipSuccess) return fail(DSA_ERR_HIP, std::string("indexer_topk_timed: hipEventRecord: ") +
+                                                          hipGetErrorString(tap.err));
+  if (n_kernels) *n_kernels = tap.n;
+  return DSA_OK;
+}
+
+dsa_status dsa_clock_probe(uint64_t* out, int64_t ticks, void* stream) {
+  clear_error();
+  if (!out || ticks < 1 || ticks > 10000000) return fail(DSA_ERR_INVALID_ARG, "clock_probe: need out and 1 <= ticks <= 1e7");
+  hipLaunchKernelGGL(clock_probe_kernel, dim3(1), dim3(64), 0, as_stream(stream), out, uint64_t(ticks));
+  return check_launch("clock_probe_kernel");
 }
 
 dsa_status dsa_sparse_attn(const dsa_sparse_attn_args* a, void* stream) {

@@ -20,6 +20,11 @@ dsa_status check_launch(const char* what);
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Kernel-boundary events of one library call (dsa_indexer_topk_timed): while a tap is set on the
+// calling thread, every launch site records the tap's next event on its stream right before it
+// launches, and the entry point records one more after the last launch. No tap: a no-op.
+void tap_launch(const char* kernel, hipStream_t stream);
+
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 // ---------------------------------------------------------------------------------------------

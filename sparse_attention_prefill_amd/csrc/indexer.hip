@@ -323,9 +323,11 @@ dsa_status launch_indexer_scores(const dsa_indexer_topk_args* a, float* scores, 
       a->k_scale, a->cu_seqlens_q, a->seqused_kv, a->cu_seqlens_kv, a->batch, stride, ratio, a->nq, a->nk, max_vis,  \
       chunk_keys, skip_le, scores, ld, a->err_flag, c.fuse_above, c.theta, c.n_cand, c.cand, c.cap
     if (a->dtype == DSA_BF16) {
+      tap_launch(cm ? "indexer_mfma<bf16,candidates>" : "indexer_mfma<bf16>", stream);
       if (cm) hipLaunchKernelGGL((indexer_mfma<false, true>), grid, dim3(kThreads), 0, stream, DSA_IDX_ARGS);
       else hipLaunchKernelGGL((indexer_mfma<false, false>), grid, dim3(kThreads), 0, stream, DSA_IDX_ARGS);
     } else {
+      tap_launch(cm ? "indexer_mfma<fp8,candidates>" : "indexer_mfma<fp8>", stream);
       if (cm) hipLaunchKernelGGL((indexer_mfma<true, true>), grid, dim3(kThreads), 0, stream, DSA_IDX_ARGS);
       else hipLaunchKernelGGL((indexer_mfma<true, false>), grid, dim3(kThreads), 0, stream, DSA_IDX_ARGS);
     }
@@ -345,6 +347,7 @@ dsa_status launch_indexer_scores(const dsa_indexer_topk_args* a, float* scores, 
                      static_cast<const T*>(a->q_idx), a->weights, static_cast<const T*>(a->k_idx), a->cu_seqlens_q, \
                      a->seqused_kv, a->cu_seqlens_kv, a->batch, stride, ratio, a->nq, a->nk, a->n_heads, D, max_vis, \
                      skip_le, scores, ld, a->err_flag)
+  if (a->dtype == DSA_F32 || a->dtype == DSA_BF16) tap_launch("indexer_generic", stream);
   if (a->dtype == DSA_F32) {
     if (kd == 32) DSA_GEN_IDX(float, 32);
     else if (kd == 64) DSA_GEN_IDX(float, 64);

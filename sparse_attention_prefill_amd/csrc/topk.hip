@@ -730,6 +730,312 @@ __global__ __launch_bounds__(kStreamNT, 8) void topk_stream_kernel(
 }
 
 // ---------------------------------------------------------------------------------------------
+// Rows of up to kSmpMaxRow keys: 256 threads per row and about 32 KB of LDS, so five rows are in
+// flight on each CU and one row's passes overlap the others' loads.
+//   * A row of at most kSmpList keys is its own list.
+//   * A longer row is sampled first: 16 tiles of 256 consecutive keys spread evenly over it give
+//     a threshold theta that about K + 4 spreads of the row's keys reach (the r-th largest of the
+//     m = 4096 sample keys, r the smallest rank whose expected count r*ev/m stays 4 binomial
+//     spreads sqrt(r)*ev/m above K). One float4 pass over the row then appends every key >= theta
+//     (its order key and 16-bit position) to the LDS list, one LDS atomic per wave per step.
+//   * The list is selected exactly, keys taken relative to the list's base key (theta, or the
+//     row's smallest key) so that the 11-bit digits spread over the list's own span; ids are
+//     emitted ascending from position bitmaps.
+//   * A list that overflowed or holds fewer than K keys (ties, adversarial rows) sends the row to
+//     an exact radix select over the row in memory (11 + 11 + 10 bits).
+// ---------------------------------------------------------------------------------------------
+constexpr int kSmpNT = 256;
+constexpr int kSmpMaxRow = 32768;
+constexpr int kSmpList = 3968;                 // list entries: 23.25 KB with 16-bit positions
+constexpr int kSmpTiles = 16, kSmpTile = 256;  // sample: 16 tiles of 256 consecutive keys
+constexpr int kSmpSample = kSmpTiles * kSmpTile;
+constexpr int kSmpBins = 2048;                 // 11-bit digits
+constexpr int kSmpU = 4;                       // float4 loads in flight per thread on the pass
+
+struct SampleShared {
+  uint32_t key[kSmpList];  // order keys of the list
+  uint16_t pos[kSmpList];  // their positions in the row
+  union {
+    alignas(16) uint32_t hist[kSmpBins];
+    uint64_t bits[2][kSmpMaxRow / 64];  // keys above tau / equal to tau, one bit per position
+  } u;
+  int scan[2 * (kSmpNT / 64 + 1)];
+  uint32_t red[2][kSmpNT / 64];
+  uint32_t prefix;   // selected digits so far (relative keys >> lo)
+  int remaining;     // keys still to take inside the prefix's bin
+  int lo;            // lowest bit the prefix covers
+  int take_all;      // every key of the prefix's bin is taken
+  int n_list;
+};
+
+// Workgroup-wide min and max of one value per thread, returned in every thread (one barrier;
+// `red` is free again after the caller's next barrier).
+__device__ inline void smp_minmax(uint32_t mn, uint32_t mx, uint32_t (*red)[kSmpNT / 64], uint32_t* omn,
+                                  uint32_t* omx) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    mn = min(mn, uint32_t(__shfl_xor(int(mn), o, 64)));
+    mx = max(mx, uint32_t(__shfl_xor(int(mx), o, 64)));
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) {
+    red[0][wave] = mn;
+    red[1][wave] = mx;
+  }
+  __syncthreads();
+  mn = red[0][0];
+  mx = red[1][0];
+#pragma unroll
+  for (int w = 1; w < kSmpNT / 64; ++w) {
+    mn = min(mn, red[0][w]);
+    mx = max(mx, red[1][w]);
+  }
+  *omn = mn;
+  *omx = mx;
+}
+
+// One wave selects in sh.u.hist the bin of the rem-th largest key and records the digit.
+__device__ inline void smp_select_digit(SampleShared& sh, uint32_t pfx, int wb, int lo, int rem) {
+  if ((threadIdx.x >> 6) == 0) {
+    int bin, r, cnt;
+    wave_select<kSmpBins>(sh.u.hist, rem, &bin, &r, &cnt);
+    if ((threadIdx.x & 63) == 0) {
+      sh.prefix = wb >= 32 ? uint32_t(bin) : (pfx << wb) | uint32_t(bin);
+      sh.remaining = r;
+      sh.take_all = r == cnt;
+      sh.lo = lo;
+    }
+  }
+}
+
+// Exact K-th largest over the n list keys, relative to `base` (every listed key >= base): the
+// first digit is the 11 bits below the highest set bit of the largest relative key, the lower
+// bits follow in digits of at most 11 bits, stopping once the chosen bin is taken whole.
+__device__ inline void smp_list_select(SampleShared& sh, int n, int K, uint32_t base) {
+  const int tid = threadIdx.x;
+  uint32_t mx = 0, mn;
+  for (int c = tid; c < n; c += kSmpNT) mx = max(mx, sh.key[c] - base);
+  smp_minmax(0u, mx, sh.red, &mn, &mx);
+  const int s1 = max(0, 32 - int(__builtin_clz(mx | 1u)) - 11);  // (d >> s1) < 2048
+  zero_words<kSmpNT>(sh.u.hist, kSmpBins);
+  __syncthreads();
+  for (int c = tid; c < n; c += kSmpNT) atomicAdd(&sh.u.hist[(sh.key[c] - base) >> s1], 1u);
+  __syncthreads();
+  smp_select_digit(sh, 0u, 32, s1, K);
+  __syncthreads();
+  int lo = s1;
+#pragma unroll 1
+  while (!sh.take_all && lo > 0) {  // uniform: read after a barrier
+    const int wb = min(11, lo);
+    lo -= wb;
+    const uint32_t pfx = sh.prefix;
+    const int rem = sh.remaining;
+    zero_words<kSmpNT>(sh.u.hist, kSmpBins);
+    __syncthreads();
+    for (int c = tid; c < n; c += kSmpNT) {
+      const uint32_t d = sh.key[c] - base;
+      if ((d >> (lo + wb)) == pfx) atomicAdd(&sh.u.hist[(d >> lo) & ((1u << wb) - 1u)], 1u);
+    }
+    __syncthreads();
+    smp_select_digit(sh, pfx, wb, lo, rem);
+    __syncthreads();
+  }
+}
+
+// The selection of the list (after smp_list_select) as ascending ids, through position bitmaps.
+__device__ inline void smp_list_emit(SampleShared& sh, int n, int ev, int K, uint32_t base, int id_base,
+                                     int32_t* __restrict__ orow) {
+  const int tid = threadIdx.x;
+  const uint32_t pfx = sh.prefix;
+  const int lo = sh.lo, need = sh.remaining;
+  const int n_chunks = (ev + 63) >> 6;
+  uint64_t* gt = sh.u.bits[0];
+  uint64_t* eq = sh.u.bits[1];
+  for (int c = tid; c < n_chunks; c += kSmpNT) gt[c] = eq[c] = 0;  // the select's reads are done
+  __syncthreads();
+  for (int c = tid; c < n; c += kSmpNT) {
+    const uint32_t d = (sh.key[c] - base) >> lo;
+    const int p = sh.pos[c];
+    if (d > pfx) atomicOr(&gt[p >> 6], 1ull << (p & 63));
+    else if (d == pfx) atomicOr(&eq[p >> 6], 1ull << (p & 63));
+  }
+  __syncthreads();
+  emit_from_bitmaps<kSmpNT>(gt, eq, n_chunks, need, K, id_base, orow, sh.scan);
+}
+
+// Exact select over the row in memory (a list that overflowed or fell short): three digits of
+// the order keys (11 + 11 + 10 bits), then the bitmaps from one more pass.
+__device__ inline void smp_row_select(const float* __restrict__ srow, int ev, int K, int id_base,
+                                      int32_t* __restrict__ orow, SampleShared& sh) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t pfx = 0;
+  int rem = K, lo = 32;
+#pragma unroll 1
+  for (int dg = 0; dg < 3; ++dg) {
+    const int wb = dg < 2 ? 11 : 10;
+    lo -= wb;
+    zero_words<kSmpNT>(sh.u.hist, kSmpBins);
+    __syncthreads();
+    for (int p = tid; p < ev; p += kSmpNT) {
+      const uint32_t key = order_key(srow[p]);
+      if (dg == 0 || (key >> (lo + wb)) == pfx) atomicAdd(&sh.u.hist[(key >> lo) & ((1u << wb) - 1u)], 1u);
+    }
+    __syncthreads();
+    smp_select_digit(sh, pfx, dg == 0 ? 32 : wb, lo, rem);
+    __syncthreads();
+    pfx = sh.prefix;
+    rem = sh.remaining;
+    if (sh.take_all) break;  // uniform
+  }
+  const int n_chunks = (ev + 63) >> 6;
+  uint64_t* gt = sh.u.bits[0];
+  uint64_t* eq = sh.u.bits[1];
+  for (int c = wave; c < n_chunks; c += kSmpNT / 64) {
+    const int p = c * 64 + lane;
+    const bool valid = p < ev;
+    const uint32_t d = valid ? order_key(srow[p]) >> lo : 0u;
+    const uint64_t g = ballot(valid && d > pfx), e = ballot(valid && d == pfx);
+    if (lane == 0) {
+      gt[c] = g;
+      eq[c] = e;
+    }
+  }
+  __syncthreads();
+  emit_from_bitmaps<kSmpNT>(gt, eq, n_chunks, rem, K, id_base, orow, sh.scan);
+}
+
+__global__ __launch_bounds__(kSmpNT, 5) void topk_sample_kernel(
+    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ used_kv,
+    const int32_t* __restrict__ cu_kv, const int32_t* __restrict__ win_kv, int batch, int stride, int ratio, int nk,
+    int max_vis, int K, int window, int kv_row_base, int32_t* __restrict__ out, int32_t* __restrict__ err_flag,
+    int skip_above) {
+  __shared__ SampleShared sh;
+  const int tid = threadIdx.x, lane = tid & 63;
+  int32_t* orow = out + int64_t(blockIdx.x) * (K + window);
+  RowInfo ri;
+  if (!row_setup<kSmpNT>(cu_q, used_kv, cu_kv, win_kv, batch, stride, ratio, nk, max_vis, kSmpMaxRow, K, window,
+                         kv_row_base, orow, err_flag, &ri, skip_above))
+    return;
+  const int ev = ri.ev;  // K < ev <= kSmpMaxRow
+  const float* srow = scores + int64_t(blockIdx.x) * ld;
+  const float4* s4 = reinterpret_cast<const float4*>(srow);  // rows are 16-byte aligned, ld % 4 == 0
+  int n;
+  uint32_t base;
+  if (ev <= kSmpList) {
+    // ---- the whole row is the list (position p at slot p) ----
+    uint32_t mn = 0xFFFFFFFFu, mx;
+    for (int q = tid; 4 * q < ev; q += kSmpNT) {
+      const float4 x = s4[q];
+      const float xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int p = 4 * q + c;
+        if (p < ev) {
+          const uint32_t k = order_key(xs[c]);
+          sh.key[p] = k;
+          sh.pos[p] = uint16_t(p);
+          mn = min(mn, k);
+        }
+      }
+    }
+    smp_minmax(mn, 0u, sh.red, &mn, &mx);
+    n = ev;
+    base = mn;
+  } else {
+    // ---- sample: 4 float4 per thread; a wave's load covers one 256-key tile ----
+    uint32_t sk[16];
+    uint32_t mn = 0xFFFFFFFFu, mx = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int f = u * kSmpNT + tid, t = f >> 6;
+      const int start = int(int64_t(t) * (ev - kSmpTile) / (kSmpTiles - 1)) & ~3;
+      const float4 x = s4[(start >> 2) + (f & 63)];
+      sk[4 * u] = order_key(x.x);
+      sk[4 * u + 1] = order_key(x.y);
+      sk[4 * u + 2] = order_key(x.z);
+      sk[4 * u + 3] = order_key(x.w);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        mn = min(mn, sk[4 * u + c]);
+        mx = max(mx, sk[4 * u + c]);
+      }
+    }
+    if (tid == 0) sh.n_list = 0;
+    smp_minmax(mn, mx, sh.red, &mn, &mx);
+    const int s1 = max(0, 32 - int(__builtin_clz((mx - mn) | 1u)) - 11);
+    zero_words<kSmpNT>(sh.u.hist, kSmpBins);
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 16; ++k) atomicAdd(&sh.u.hist[(sk[k] - mn) >> s1], 1u);
+    __syncthreads();
+    // r: smallest rank with r * ev / m - 4 sqrt(r) * ev / m >= K
+    const float y = 2.f + sqrtf(4.f + float(K) * float(kSmpSample) / float(ev));
+    const int r = min(kSmpSample, int(ceilf(y * y)));
+    if ((tid >> 6) == 0) {
+      int bin, rem, cnt;
+      wave_select<kSmpBins>(sh.u.hist, r, &bin, &rem, &cnt);
+      if (lane == 0) sh.prefix = mn + (uint32_t(bin) << s1);
+    }
+    __syncthreads();
+    base = sh.prefix;  // theta as an order key
+    // ---- one pass: list every key >= theta. A normal theta compares as a float (the same order
+    // for every float, denormals included, -0 == +0); otherwise the order keys are compared. ----
+    const float theta = key_to_float(base);
+    const bool by_float = fabsf(theta) >= 1.17549435e-38f;
+    const int n4 = (ev + 3) >> 2;
+#pragma unroll 1
+    for (int v0 = 0; v0 < n4; v0 += kSmpNT * kSmpU) {
+      float4 x[kSmpU];
+#pragma unroll
+      for (int u = 0; u < kSmpU; ++u) {
+        const int q = v0 + u * kSmpNT + tid;
+        x[u] = q < n4 ? s4[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      const bool full = 4 * (v0 + kSmpNT * kSmpU) <= ev;  // uniform: every position of the step is in the row
+      auto hit = [&](int u, int c) {
+        const float xc = c == 0 ? x[u].x : c == 1 ? x[u].y : c == 2 ? x[u].z : x[u].w;
+        const bool in = full || 4 * (v0 + u * kSmpNT + tid) + c < ev;
+        return in && (by_float ? xc >= theta : order_key(xc) >= base);
+      };
+      uint64_t m[kSmpU][4];
+      int total = 0;
+#pragma unroll
+      for (int u = 0; u < kSmpU; ++u)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          m[u][c] = ballot(hit(u, c));
+          total += __popcll(m[u][c]);
+        }
+      if (total == 0) continue;  // uniform per wave
+      int slot = 0;
+      if (lane == 0) slot = atomicAdd(&sh.n_list, total);
+      slot = __builtin_amdgcn_readfirstlane(slot);
+#pragma unroll
+      for (int u = 0; u < kSmpU; ++u)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int sl = slot + lanes_below(m[u][c]);
+          if (((m[u][c] >> lane) & 1ull) && sl < kSmpList) {
+            const float xc = c == 0 ? x[u].x : c == 1 ? x[u].y : c == 2 ? x[u].z : x[u].w;
+            sh.key[sl] = order_key(xc);
+            sh.pos[sl] = uint16_t(4 * (v0 + u * kSmpNT + tid) + c);
+          }
+          slot += __popcll(m[u][c]);
+        }
+    }
+    __syncthreads();
+    n = sh.n_list;
+  }
+  if (n >= K && n <= kSmpList) {  // uniform
+    smp_list_select(sh, n, K, base);
+    smp_list_emit(sh, n, ev, K, base, ri.base, orow);
+  } else {
+    __syncthreads();
+    smp_row_select(srow, ev, K, ri.base, orow, sh);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
 // Rows selected from candidate lists (no score row in memory)
 // ---------------------------------------------------------------------------------------------
 constexpr int kThetaBins = 2048;                       // 11-bit digits of the sample select
@@ -1070,10 +1376,8 @@ dsa_status launch_topk(const dsa_indexer_topk_args* a, const float* scores, int6
   scores, ld, a->cu_seqlens_q, a->seqused_kv, a->cu_seqlens_kv, a->window_kv_start, a->batch, a->q_stride,     \
       a->compress_ratio, a->nk, max_vis, a->topk, a->window, a->kv_row_base, a->topk_idx, a->err_flag, INT32_MAX
 #define DSA_TOPK_REG(NT, E) hipLaunchKernelGGL((topk_reg_kernel<NT, E>), grid, dim3(NT), 0, stream, DSA_TOPK_ARGS)
-  if (max_vis <= 256 * 16) DSA_TOPK_REG(256, 16);
-  else if (max_vis <= 512 * 16) DSA_TOPK_REG(512, 16);
-  else if (max_vis <= 1024 * 16) DSA_TOPK_REG(1024, 16);
-  else if (max_vis <= 1024 * 32) DSA_TOPK_REG(1024, 32);
+  tap_launch(max_vis <= kSmpMaxRow ? "topk_sample_kernel" : "topk_stream_kernel", stream);
+  if (max_vis <= kSmpMaxRow) hipLaunchKernelGGL(topk_sample_kernel, grid, dim3(kSmpNT), 0, stream, DSA_TOPK_ARGS);
   else hipLaunchKernelGGL(topk_stream_kernel, grid, dim3(kStreamNT), 0, stream, DSA_TOPK_ARGS);
 #undef DSA_TOPK_REG
 #undef DSA_TOPK_ARGS
@@ -1090,6 +1394,7 @@ dsa_status launch_topk_theta(const dsa_indexer_topk_args* a, int max_vis, const 
   static_cast<const unsigned char*>(a->q_idx), a->q_scale, a->weights, static_cast<const unsigned char*>(a->k_idx), \
       a->k_scale, a->cu_seqlens_q, a->seqused_kv, a->cu_seqlens_kv, a->batch, a->q_stride, a->compress_ratio, a->nq, \
       a->nk, max_vis, a->topk, cm.fuse_above, cm.theta, cm.n_cand, cm.segs
+  tap_launch("topk_theta_kernel", stream);
   if (a->dtype == DSA_FP8_E4M3) hipLaunchKernelGGL(topk_theta_kernel<true>, grid, dim3(512), 0, stream, DSA_THETA_ARGS);
   else hipLaunchKernelGGL(topk_theta_kernel<false>, grid, dim3(512), 0, stream, DSA_THETA_ARGS);
 #undef DSA_THETA_ARGS
@@ -1102,11 +1407,13 @@ dsa_status launch_topk_candidates(const dsa_indexer_topk_args* a, const float* s
   if (a->nq == 0) return DSA_OK;
   if (max_vis > kMaxRow) return fail(DSA_ERR_UNSUPPORTED, "topk: rows longer than 131072 keys");
   const dim3 grid(a->nq);
+  tap_launch("topk_reg_kernel", stream);
   hipLaunchKernelGGL((topk_reg_kernel<1024, 32>), grid, dim3(1024), 0, stream, score_rows, ld, a->cu_seqlens_q,
                      a->seqused_kv, a->cu_seqlens_kv, a->window_kv_start, a->batch, a->q_stride, a->compress_ratio,
                      a->nk, max_vis, a->topk, a->window, a->kv_row_base, a->topk_idx, a->err_flag, cm.fuse_above);
   dsa_status st = check_launch("topk_reg_kernel");
   if (st != DSA_OK) return st;
+  tap_launch("topk_cand_kernel", stream);
   hipLaunchKernelGGL(topk_cand_kernel, grid, dim3(kCandNT), 0, stream, cm.cand, cm.n_cand, cm.status, cm.theta,
                      cm.cap, cm.segs, cm.fuse_above,
                      a->cu_seqlens_q, a->seqused_kv, a->cu_seqlens_kv, a->window_kv_start, a->batch, a->q_stride,
@@ -1118,6 +1425,7 @@ dsa_status launch_topk_candidates(const dsa_indexer_topk_args* a, const float* s
       a->k_scale, a->cu_seqlens_q, a->seqused_kv, a->cu_seqlens_kv, a->batch, a->q_stride, a->compress_ratio, a->nq, \
       a->nk, max_vis, a->topk, a->window, a->kv_row_base, cm.fuse_above, cm.status, scratch, sld, a->topk_idx
   const dim3 rgrid(n_scratch);
+  tap_launch("topk_refill_kernel", stream);
   if (a->dtype == DSA_FP8_E4M3) hipLaunchKernelGGL(topk_refill_kernel<true>, rgrid, dim3(kStreamNT), 0, stream, DSA_REFILL_ARGS);
   else hipLaunchKernelGGL(topk_refill_kernel<false>, rgrid, dim3(kStreamNT), 0, stream, DSA_REFILL_ARGS);
 #undef DSA_REFILL_ARGS

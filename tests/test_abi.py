@@ -127,3 +127,14 @@ def test_binding_rejects_tensors_the_library_cannot_read():
                       None, 0.1, 512)
     with pytest.raises(D.DsaError, match="GPU|contiguous"):
         D.rerange(torch.zeros(8, 64, dtype=torch.bfloat16)[:, ::2], 8, 2, 1, False)
+
+
+def test_timed_indexer_rejects_missing_events_before_launch():
+    import sparse_attention_prefill_amd as D
+    L = D.lib()
+    g = D.binding.IndexerArgs()
+    n = ctypes.c_int32(-1)
+    assert L.dsa_indexer_topk_timed(ctypes.byref(g), None, None, 4, ctypes.byref(n), None) == 1
+    ev = (ctypes.c_void_p * 3)(16, None, 32)
+    assert L.dsa_indexer_topk_timed(ctypes.byref(g), None, ev, 3, ctypes.byref(n), None) == 1
+    assert b"NULL event" in L.dsa_last_error() and n.value == -1

@@ -117,7 +117,7 @@ def test_rows_outside_the_key_buffer_are_cleared_and_flagged(name, kw):
     outs, errs = [], []
     for k_idx in (k_full, k_full[:nk_short]):
         err = torch.zeros(1, dtype=torch.int32, device=dev)
-        out = torch.full((len(toks), wl.k_tot), 777, dtype=torch.int32, device=dev)
+        out = torch.full((len(toks), wl.k_tot), -7, dtype=torch.int32, device=dev)  # no valid entry is -7
         print(f"case {name} nk={k_idx.shape[0]} nq={len(toks)}", flush=True)
         D.indexer_topk(to_dev(qin["q_idx"], ik, dev), to_dev(qin["w"], "f32", dev), to_dev(k_idx, ik, dev),
                        to_dev(m["local_query_start_loc"], "i32", dev), to_dev(m["local_seq_lens"], "i32", dev),
@@ -130,4 +130,4 @@ def test_rows_outside_the_key_buffer_are_cleared_and_flagged(name, kw):
     assert errs[0] == 0 and errs[1] & 0x20
     assert np.all(outs[1][bad] == -1)
     assert np.array_equal(outs[1][~bad], outs[0][~bad])
-    assert not np.any(outs[0] == 777)
+    assert not np.any(outs[0] == -7) and not np.any(outs[1] == -7)

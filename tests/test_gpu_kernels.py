@@ -10,7 +10,7 @@ import torch
 
 import oracle as O
 import synthetic as S
-from dsa_testlib import gpu, to_dev, to_f64, assert_attn_close
+from dsa_testlib import gpu, to_dev, to_f64, assert_attn_close, SCORE_TOL
 
 pytestmark = pytest.mark.gpu
 
@@ -22,13 +22,16 @@ def _meta_dev(lens, cp, rank, mode, dev):
     return m, d
 
 
-def _run_topk(scores, m, d, K, dev, ratio=1, window=0, win_start=None, kv_row_base=0):
+def _run_topk(scores, m, d, K, dev, ratio=1, window=0, win_start=None, kv_row_base=0, nk=None):
+    """Top-k of given score rows. The indexer inputs are unused placeholders, except that k_idx
+    has the nk rows (default: the KV stream's) every row's extent must fit, as for the indexer."""
     import sparse_attention_prefill_amd as D
     nq = m["n_local_real"]
     ld = scores.shape[1]
     max_kv = int(m["local_seq_lens"].max())
+    nk = max(1, int(m["local_kv_start_loc"][-1]) if nk is None else nk)
     dummy_q = torch.zeros(nq, 1, 8, dtype=torch.float32, device=dev)
-    dummy_k = torch.zeros(1, 8, dtype=torch.float32, device=dev)
+    dummy_k = torch.zeros(nk, 8, dtype=torch.float32, device=dev)
     err = torch.zeros(1, dtype=torch.int32, device=dev)
     dummy_w = torch.zeros(nq, 1, dtype=torch.float32, device=dev)
     out = D.topk_from_scores(dummy_q, dummy_w, dummy_k, d["local_query_start_loc"], d["local_seq_lens"],
@@ -83,7 +86,8 @@ def test_topk_compressed_and_window():
     ld = (max(E // 4 for _, E, _ in views) + 4) // 4 * 4
     scores = S.score_rows(77, len(views), ld, "ties")
     K = 64
-    got = _run_topk(scores, m, d, K, dev, ratio=4, window=128, win_start=to_dev(qsl, "i32", dev), kv_row_base=T)
+    got = _run_topk(scores, m, d, K, dev, ratio=4, window=128, win_start=to_dev(qsl, "i32", dev), kv_row_base=T,
+                    nk=int(ccs[-1]))
     for i, (b, E, _) in enumerate(views):
         want = T + ccs[b] + O.topk_positions(scores[i, :E // 4], K)
         assert np.array_equal(got[i, :len(want)], want) and np.all(got[i, len(want):K] == -1), i
@@ -132,8 +136,7 @@ def _indexer_case(wl, variant, dev, rows_cap=None):
             assert np.array_equal(g, ref), (wl.name, i)
             assert not np.any(np.signbit(g[g == 0])), "negative zero score"
         else:
-            # fp8 MFMA sums are measured within ~2e-5 of the row maximum, not fp32-exact
-            tol = (1e-4 if wl.idx_dtype == "fp8" else 2e-5) * max(np.abs(ref).max(), 1e-30)
+            tol = SCORE_TOL[wl.idx_dtype] * max(np.abs(ref).max(), 1e-30)
             assert np.abs(g - ref).max() <= tol, (wl.name, i, np.abs(g - ref).max(), tol)
 
 
