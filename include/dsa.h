@@ -182,6 +182,17 @@ dsa_status dsa_indexer_scores(const dsa_indexer_topk_args* args, float* scores, 
 dsa_status dsa_topk_from_scores(const dsa_indexer_topk_args* args, const float* scores,
                                 int64_t ld, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): dsa_indexer_topk with the library's own scratch instead
+ * of args->workspace (ignored). The scratch is a static 64 MiB device array, one copy per GPU the
+ * library runs on, held until the process ends; the call allocates nothing. Every call on a GPU
+ * shares that GPU's copy, so calls that overlap on one GPU (other streams, other host threads)
+ * race and give wrong results: serialise them. The scratch keeps the previous call's contents;
+ * nothing in it needs to start at zero. `stream` must belong to the current device.
+ * Errors: those of dsa_indexer_topk; DSA_ERR_WORKSPACE (before any launch) when
+ * dsa_indexer_topk_workspace() of the call exceeds 64 MiB (e.g. more than ~16M score entries). */
+dsa_status dsa_indexer_topk_noalloc(const dsa_indexer_topk_args* args, void* stream);
+
 /* Measurement hook, for benchmarks and profilers that time the kernels inside one call:
  * dsa_indexer_topk(args, stream), with events[k] recorded on `stream` right before the k-th
  * kernel the call launches and events[n] right after the last one, n = *n_kernels (out), so

@@ -59,6 +59,7 @@ def lib():
         L.dsa_indexer_topk_workspace.argtypes = [ctypes.POINTER(IndexerArgs)]
         L.dsa_indexer_topk_workspace.restype = c_size
         L.dsa_indexer_topk.argtypes = [ctypes.POINTER(IndexerArgs), c_p]
+        L.dsa_indexer_topk_noalloc.argtypes = [ctypes.POINTER(IndexerArgs), c_p]
         L.dsa_indexer_topk_timed.argtypes = [ctypes.POINTER(IndexerArgs), c_p, ctypes.POINTER(c_p), c_i32,
                                              ctypes.POINTER(c_i32), ctypes.POINTER(ctypes.c_char_p)]
         L.dsa_indexer_scores.argtypes = [ctypes.POINTER(IndexerArgs), c_p, c_i64, c_p]
@@ -66,7 +67,8 @@ def lib():
         L.dsa_sparse_attn.argtypes = [ctypes.POINTER(AttnArgs), c_p]
         L.dsa_clock_probe.argtypes = [c_p, c_i64, c_p]
         L.dsa_rerange.argtypes = [c_p, c_p, c_i32, c_i64, c_i32, c_i32, c_i32, c_i32, c_p]
-        for f in ("dsa_cp_sizes", "dsa_build_cp_metadata", "dsa_indexer_topk", "dsa_indexer_topk_timed",
+        for f in ("dsa_cp_sizes", "dsa_build_cp_metadata", "dsa_indexer_topk", "dsa_indexer_topk_noalloc",
+                  "dsa_indexer_topk_timed",
                   "dsa_indexer_scores",
                   "dsa_topk_from_scores", "dsa_sparse_attn", "dsa_rerange", "dsa_clock_probe"):
             getattr(L, f).restype = c_i32
@@ -218,6 +220,19 @@ def indexer_topk(q_idx, weights, k_idx, cu_seqlens_q, seqused_kv, cu_seqlens_kv,
     a = _indexer_args(q_idx, weights, k_idx, cu_seqlens_q, seqused_kv, cu_seqlens_kv, max_seqlen_kv,
                       topk_idx=topk_idx, workspace=workspace, **kw)
     _check(lib().dsa_indexer_topk(ctypes.byref(a), _stream(stream)), "dsa_indexer_topk")
+    return topk_idx
+
+
+def indexer_topk_noalloc(q_idx, weights, k_idx, cu_seqlens_q, seqused_kv, cu_seqlens_kv, max_seqlen_kv, topk_idx,
+                         stream=None, **kw):
+    """indexer_topk for callers that cannot allocate: the library's static per-GPU scratch (64 MiB)
+    instead of a workspace; topk_idx [nq, topk + window] int32 must be given. Calls that overlap on
+    one GPU race. Allocates nothing."""
+    if topk_idx is None:
+        raise DsaError("indexer_topk_noalloc: topk_idx must be given (this call allocates nothing)")
+    a = _indexer_args(q_idx, weights, k_idx, cu_seqlens_q, seqused_kv, cu_seqlens_kv, max_seqlen_kv,
+                      topk_idx=topk_idx, **kw)
+    _check(lib().dsa_indexer_topk_noalloc(ctypes.byref(a), _stream(stream)), "dsa_indexer_topk_noalloc")
     return topk_idx
 
 

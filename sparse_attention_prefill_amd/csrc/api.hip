@@ -2,9 +2,14 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 
 #include "dsa_internal.h"
+
+// Scratch of dsa_indexer_topk_noalloc (see static_scratch below): 64 MiB per GPU.
+static constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
 
 namespace dsa {
 
@@ -140,6 +145,40 @@ dsa_status check_indexer_args(const dsa_indexer_topk_args* a, bool need_out) {
   return DSA_OK;
 }
 
+// ---------------------------------------------------------------------------------------------
+// Scratch of dsa_indexer_topk_noalloc, for callers that cannot allocate: a file-scope device array,
+// one copy per GPU the library runs on, held until the process ends. Host code never uses the
+// array's name as an address: the device's copy is found once per device with
+// hipGetSymbolAddress, with that device current, and that address is what the kernels receive.
+// ---------------------------------------------------------------------------------------------
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices];
+
+dsa_status static_scratch(hipStream_t stream, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(DSA_ERR_HIP, std::string("indexer_topk_noalloc: hipGetDevice: ") + hipGetErrorString(e));
+  if (stream) {
+    hipDevice_t sdev = -1;
+    e = hipStreamGetDevice(stream, &sdev);
+    if (e != hipSuccess)
+      return fail(DSA_ERR_HIP, std::string("indexer_topk_noalloc: hipStreamGetDevice: ") + hipGetErrorString(e));
+    if (int(sdev) != dev) return fail(DSA_ERR_INVALID_ARG, "indexer_topk_noalloc: the stream is not on the current device");
+  }
+  if (dev < 0 || dev >= kMaxScratchDevices) return fail(DSA_ERR_UNSUPPORTED, "indexer_topk_noalloc: device id too large");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(DSA_ERR_HIP, std::string("indexer_topk_noalloc: hipGetSymbolAddress: ") + hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DSA_OK;
+}
+
 size_t workspace_need(const dsa_indexer_topk_args* a) {
   return candidate_mode(a) ? cand_layout(a).total : size_t(a->nq) * size_t(score_ld(a)) * sizeof(float);
 }
@@ -254,6 +293,25 @@ dsa_status dsa_indexer_topk(const dsa_indexer_topk_args* a, void* stream) {
     return fail(DSA_ERR_WORKSPACE, "indexer_topk: workspace missing, not 256-byte aligned or smaller than "
                                        "dsa_indexer_topk_workspace()");
   return run_indexer_topk(a, as_stream(stream));
+}
+
+dsa_status dsa_indexer_topk_noalloc(const dsa_indexer_topk_args* a, void* stream) {
+  clear_error();
+  dsa_status st = check_indexer_args(a, true);
+  if (st != DSA_OK) return st;
+  if (a->nq == 0) return DSA_OK;
+  const size_t need = workspace_need(a);
+  if (need > kStaticScratchBytes)
+    return fail(DSA_ERR_WORKSPACE, "indexer_topk_noalloc: the call needs " + std::to_string(need) +
+                                       " bytes of scratch; the static scratch holds " +
+                                       std::to_string(kStaticScratchBytes) + " (use dsa_indexer_topk with a workspace)");
+  void* ptr = nullptr;
+  st = static_scratch(as_stream(stream), &ptr);
+  if (st != DSA_OK) return st;
+  dsa_indexer_topk_args b = *a;
+  b.workspace = ptr;
+  b.workspace_bytes = kStaticScratchBytes;
+  return run_indexer_topk(&b, as_stream(stream));
 }
 
 dsa_status dsa_indexer_topk_timed(const dsa_indexer_topk_args* a, void* stream, void* const* events,
