@@ -58,6 +58,28 @@ __device__ inline int wave_incl_scan(int v) {
   return v;
 }
 
+// Max / min over the 64 lanes of a wave on DPP, in the order of wave_incl_scan (lane 63 ends with
+// the result, returned uniform). Shifted-in lanes contribute 0 to the max and the lane's own
+// value to the min.
+__device__ inline uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x111, 0xf, 0xf, true)));
+  v = max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x112, 0xf, 0xf, true)));
+  v = max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x114, 0xf, 0xf, true)));
+  v = max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x118, 0xf, 0xf, true)));
+  v = max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x142, 0xa, 0xf, false)));
+  v = max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x143, 0xc, 0xf, false)));
+  return uint32_t(__builtin_amdgcn_readlane(int(v), 63));
+}
+__device__ inline uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, uint32_t(__builtin_amdgcn_update_dpp(int(v), int(v), 0x111, 0xf, 0xf, false)));
+  v = min(v, uint32_t(__builtin_amdgcn_update_dpp(int(v), int(v), 0x112, 0xf, 0xf, false)));
+  v = min(v, uint32_t(__builtin_amdgcn_update_dpp(int(v), int(v), 0x114, 0xf, 0xf, false)));
+  v = min(v, uint32_t(__builtin_amdgcn_update_dpp(int(v), int(v), 0x118, 0xf, 0xf, false)));
+  v = min(v, uint32_t(__builtin_amdgcn_update_dpp(int(v), int(v), 0x142, 0xa, 0xf, false)));
+  v = min(v, uint32_t(__builtin_amdgcn_update_dpp(int(v), int(v), 0x143, 0xc, 0xf, false)));
+  return uint32_t(__builtin_amdgcn_readlane(int(v), 63));
+}
+
 // Exclusive block scan of one int per thread (NW waves); *total = block sum.
 template <int NW>
 __device__ inline int block_excl_scan(int v, int* smem, int* total) {
@@ -744,14 +766,14 @@ __global__ __launch_bounds__(kStreamNT, 8) void topk_stream_kernel(
 //   * A list that overflowed or holds fewer than K keys (ties, adversarial rows) sends the row to
 //     an exact radix select over the row in memory (11 + 11 + 10 bits).
 // ---------------------------------------------------------------------------------------------
-constexpr int kSmpNT = 256;
 constexpr int kSmpMaxRow = 32768;
-constexpr int kSmpList = 3968;                 // list entries: 23.25 KB with 16-bit positions
+constexpr int kSmpList = 3584;                 // list entries: 21 KB with 16-bit positions
 constexpr int kSmpTiles = 16, kSmpTile = 256;  // sample: 16 tiles of 256 consecutive keys
 constexpr int kSmpSample = kSmpTiles * kSmpTile;
 constexpr int kSmpBins = 2048;                 // 11-bit digits
-constexpr int kSmpU = 4;                       // float4 loads in flight per thread on the pass
+constexpr int kSmpInFlight = 2048;             // float4 loads in flight per workgroup on the pass (32 KB)
 
+template <int NT>
 struct SampleShared {
   uint32_t key[kSmpList];  // order keys of the list
   uint16_t pos[kSmpList];  // their positions in the row
@@ -759,24 +781,24 @@ struct SampleShared {
     alignas(16) uint32_t hist[kSmpBins];
     uint64_t bits[2][kSmpMaxRow / 64];  // keys above tau / equal to tau, one bit per position
   } u;
-  int scan[2 * (kSmpNT / 64 + 1)];
-  uint32_t red[2][kSmpNT / 64];
+  int scan[2 * (NT / 64 + 1)];
+  uint32_t red[2][NT / 64];
   uint32_t prefix;   // selected digits so far (relative keys >> lo)
   int remaining;     // keys still to take inside the prefix's bin
   int lo;            // lowest bit the prefix covers
   int take_all;      // every key of the prefix's bin is taken
+  int count;         // keys in the prefix's bin
+  int n_small;       // keys of that bin gathered for the single-wave finish
   int n_list;
 };
 
 // Workgroup-wide min and max of one value per thread, returned in every thread (one barrier;
 // `red` is free again after the caller's next barrier).
-__device__ inline void smp_minmax(uint32_t mn, uint32_t mx, uint32_t (*red)[kSmpNT / 64], uint32_t* omn,
+template <int NT>
+__device__ inline void smp_minmax(uint32_t mn, uint32_t mx, uint32_t (*red)[NT / 64], uint32_t* omn,
                                   uint32_t* omx) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    mn = min(mn, uint32_t(__shfl_xor(int(mn), o, 64)));
-    mx = max(mx, uint32_t(__shfl_xor(int(mx), o, 64)));
-  }
+  mn = wave_min_u32(mn);
+  mx = wave_max_u32(mx);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (lane == 0) {
     red[0][wave] = mn;
@@ -786,7 +808,7 @@ __device__ inline void smp_minmax(uint32_t mn, uint32_t mx, uint32_t (*red)[kSmp
   mn = red[0][0];
   mx = red[1][0];
 #pragma unroll
-  for (int w = 1; w < kSmpNT / 64; ++w) {
+  for (int w = 1; w < NT / 64; ++w) {
     mn = min(mn, red[0][w]);
     mx = max(mx, red[1][w]);
   }
@@ -795,7 +817,8 @@ __device__ inline void smp_minmax(uint32_t mn, uint32_t mx, uint32_t (*red)[kSmp
 }
 
 // One wave selects in sh.u.hist the bin of the rem-th largest key and records the digit.
-__device__ inline void smp_select_digit(SampleShared& sh, uint32_t pfx, int wb, int lo, int rem) {
+template <int NT>
+__device__ inline void smp_select_digit(SampleShared<NT>& sh, uint32_t pfx, int wb, int lo, int rem) {
   if ((threadIdx.x >> 6) == 0) {
     int bin, r, cnt;
     wave_select<kSmpBins>(sh.u.hist, rem, &bin, &r, &cnt);
@@ -803,6 +826,8 @@ __device__ inline void smp_select_digit(SampleShared& sh, uint32_t pfx, int wb, 
       sh.prefix = wb >= 32 ? uint32_t(bin) : (pfx << wb) | uint32_t(bin);
       sh.remaining = r;
       sh.take_all = r == cnt;
+      sh.count = cnt;
+      sh.n_small = 0;
       sh.lo = lo;
     }
   }
@@ -811,18 +836,49 @@ __device__ inline void smp_select_digit(SampleShared& sh, uint32_t pfx, int wb, 
 // Exact K-th largest over the n list keys, relative to `base` (every listed key >= base): the
 // first digit is the 11 bits below the highest set bit of the largest relative key, the lower
 // bits follow in digits of at most 11 bits, stopping once the chosen bin is taken whole.
-__device__ inline void smp_list_select(SampleShared& sh, int n, int K, uint32_t base) {
+template <int NT>
+__device__ inline void smp_list_select(SampleShared<NT>& sh, int n, int K, uint32_t base) {
   const int tid = threadIdx.x;
   uint32_t mx = 0, mn;
-  for (int c = tid; c < n; c += kSmpNT) mx = max(mx, sh.key[c] - base);
-  smp_minmax(0u, mx, sh.red, &mn, &mx);
+  for (int c = tid; c < n; c += NT) mx = max(mx, sh.key[c] - base);
+  smp_minmax<NT>(0u, mx, sh.red, &mn, &mx);
   const int s1 = max(0, 32 - int(__builtin_clz(mx | 1u)) - 11);  // (d >> s1) < 2048
-  zero_words<kSmpNT>(sh.u.hist, kSmpBins);
+  zero_words<NT>(sh.u.hist, kSmpBins);
   __syncthreads();
-  for (int c = tid; c < n; c += kSmpNT) atomicAdd(&sh.u.hist[(sh.key[c] - base) >> s1], 1u);
+  for (int c = tid; c < n; c += NT) atomicAdd(&sh.u.hist[(sh.key[c] - base) >> s1], 1u);
   __syncthreads();
   smp_select_digit(sh, 0u, 32, s1, K);
   __syncthreads();
+  if (!sh.take_all && s1 > 0 && sh.count <= 64) {  // uniform
+    // The chosen bin holds at most 64 keys: gather them (relative key, position) and let one wave
+    // find the rem-th largest exactly; the ties at it are then resolved by position on emission.
+    const uint32_t b = sh.prefix;
+    uint32_t* small_d = sh.u.hist;
+    for (int c = tid; c < n; c += NT) {
+      const uint32_t d = sh.key[c] - base;
+      if ((d >> s1) == b) small_d[atomicAdd(&sh.n_small, 1)] = d;
+    }
+    __syncthreads();
+    if ((tid >> 6) == 0) {
+      const int lane = tid & 63, m = sh.n_small, rem = sh.remaining;
+      const uint32_t d = lane < m ? small_d[lane] : 0u;
+      int gt = 0, ge = 0;
+      for (int j = 0; j < m; ++j) {
+        const uint32_t dj = __builtin_amdgcn_readlane(d, j);
+        gt += dj > d;
+        ge += dj >= d;
+      }
+      const uint64_t hit = ballot(lane < m && gt < rem && rem <= ge);
+      const int l = int(__builtin_ctzll(hit | (1ull << 63)));
+      if (lane == l) {
+        sh.prefix = d;  // the whole relative key
+        sh.remaining = rem - gt;
+        sh.lo = 0;
+      }
+    }
+    __syncthreads();
+    return;
+  }
   int lo = s1;
 #pragma unroll 1
   while (!sh.take_all && lo > 0) {  // uniform: read after a barrier
@@ -830,9 +886,9 @@ __device__ inline void smp_list_select(SampleShared& sh, int n, int K, uint32_t 
     lo -= wb;
     const uint32_t pfx = sh.prefix;
     const int rem = sh.remaining;
-    zero_words<kSmpNT>(sh.u.hist, kSmpBins);
+    zero_words<NT>(sh.u.hist, kSmpBins);
     __syncthreads();
-    for (int c = tid; c < n; c += kSmpNT) {
+    for (int c = tid; c < n; c += NT) {
       const uint32_t d = sh.key[c] - base;
       if ((d >> (lo + wb)) == pfx) atomicAdd(&sh.u.hist[(d >> lo) & ((1u << wb) - 1u)], 1u);
     }
@@ -843,7 +899,8 @@ __device__ inline void smp_list_select(SampleShared& sh, int n, int K, uint32_t 
 }
 
 // The selection of the list (after smp_list_select) as ascending ids, through position bitmaps.
-__device__ inline void smp_list_emit(SampleShared& sh, int n, int ev, int K, uint32_t base, int id_base,
+template <int NT>
+__device__ inline void smp_list_emit(SampleShared<NT>& sh, int n, int ev, int K, uint32_t base, int id_base,
                                      int32_t* __restrict__ orow) {
   const int tid = threadIdx.x;
   const uint32_t pfx = sh.prefix;
@@ -851,22 +908,23 @@ __device__ inline void smp_list_emit(SampleShared& sh, int n, int ev, int K, uin
   const int n_chunks = (ev + 63) >> 6;
   uint64_t* gt = sh.u.bits[0];
   uint64_t* eq = sh.u.bits[1];
-  for (int c = tid; c < n_chunks; c += kSmpNT) gt[c] = eq[c] = 0;  // the select's reads are done
+  for (int c = tid; c < n_chunks; c += NT) gt[c] = eq[c] = 0;  // the select's reads are done
   __syncthreads();
-  for (int c = tid; c < n; c += kSmpNT) {
+  for (int c = tid; c < n; c += NT) {
     const uint32_t d = (sh.key[c] - base) >> lo;
     const int p = sh.pos[c];
     if (d > pfx) atomicOr(&gt[p >> 6], 1ull << (p & 63));
     else if (d == pfx) atomicOr(&eq[p >> 6], 1ull << (p & 63));
   }
   __syncthreads();
-  emit_from_bitmaps<kSmpNT>(gt, eq, n_chunks, need, K, id_base, orow, sh.scan);
+  emit_from_bitmaps<NT>(gt, eq, n_chunks, need, K, id_base, orow, sh.scan);
 }
 
 // Exact select over the row in memory (a list that overflowed or fell short): three digits of
 // the order keys (11 + 11 + 10 bits), then the bitmaps from one more pass.
+template <int NT>
 __device__ inline void smp_row_select(const float* __restrict__ srow, int ev, int K, int id_base,
-                                      int32_t* __restrict__ orow, SampleShared& sh) {
+                                      int32_t* __restrict__ orow, SampleShared<NT>& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t pfx = 0;
   int rem = K, lo = 32;
@@ -874,9 +932,9 @@ __device__ inline void smp_row_select(const float* __restrict__ srow, int ev, in
   for (int dg = 0; dg < 3; ++dg) {
     const int wb = dg < 2 ? 11 : 10;
     lo -= wb;
-    zero_words<kSmpNT>(sh.u.hist, kSmpBins);
+    zero_words<NT>(sh.u.hist, kSmpBins);
     __syncthreads();
-    for (int p = tid; p < ev; p += kSmpNT) {
+    for (int p = tid; p < ev; p += NT) {
       const uint32_t key = order_key(srow[p]);
       if (dg == 0 || (key >> (lo + wb)) == pfx) atomicAdd(&sh.u.hist[(key >> lo) & ((1u << wb) - 1u)], 1u);
     }
@@ -890,7 +948,7 @@ __device__ inline void smp_row_select(const float* __restrict__ srow, int ev, in
   const int n_chunks = (ev + 63) >> 6;
   uint64_t* gt = sh.u.bits[0];
   uint64_t* eq = sh.u.bits[1];
-  for (int c = wave; c < n_chunks; c += kSmpNT / 64) {
+  for (int c = wave; c < n_chunks; c += NT / 64) {
     const int p = c * 64 + lane;
     const bool valid = p < ev;
     const uint32_t d = valid ? order_key(srow[p]) >> lo : 0u;
@@ -901,19 +959,21 @@ __device__ inline void smp_row_select(const float* __restrict__ srow, int ev, in
     }
   }
   __syncthreads();
-  emit_from_bitmaps<kSmpNT>(gt, eq, n_chunks, rem, K, id_base, orow, sh.scan);
+  emit_from_bitmaps<NT>(gt, eq, n_chunks, rem, K, id_base, orow, sh.scan);
 }
 
-__global__ __launch_bounds__(kSmpNT, 5) void topk_sample_kernel(
+// NT threads per row (256: five rows per CU).
+template <int NT>
+__global__ __launch_bounds__(NT, NT == 256 ? 5 : 8) void topk_sample_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ used_kv,
     const int32_t* __restrict__ cu_kv, const int32_t* __restrict__ win_kv, int batch, int stride, int ratio, int nk,
     int max_vis, int K, int window, int kv_row_base, int32_t* __restrict__ out, int32_t* __restrict__ err_flag,
     int skip_above) {
-  __shared__ SampleShared sh;
+  __shared__ SampleShared<NT> sh;
   const int tid = threadIdx.x, lane = tid & 63;
   int32_t* orow = out + int64_t(blockIdx.x) * (K + window);
   RowInfo ri;
-  if (!row_setup<kSmpNT>(cu_q, used_kv, cu_kv, win_kv, batch, stride, ratio, nk, max_vis, kSmpMaxRow, K, window,
+  if (!row_setup<NT>(cu_q, used_kv, cu_kv, win_kv, batch, stride, ratio, nk, max_vis, kSmpMaxRow, K, window,
                          kv_row_base, orow, err_flag, &ri, skip_above))
     return;
   const int ev = ri.ev;  // K < ev <= kSmpMaxRow
@@ -924,7 +984,7 @@ __global__ __launch_bounds__(kSmpNT, 5) void topk_sample_kernel(
   if (ev <= kSmpList) {
     // ---- the whole row is the list (position p at slot p) ----
     uint32_t mn = 0xFFFFFFFFu, mx;
-    for (int q = tid; 4 * q < ev; q += kSmpNT) {
+    for (int q = tid; 4 * q < ev; q += NT) {
       const float4 x = s4[q];
       const float xs[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
@@ -938,35 +998,33 @@ __global__ __launch_bounds__(kSmpNT, 5) void topk_sample_kernel(
         }
       }
     }
-    smp_minmax(mn, 0u, sh.red, &mn, &mx);
+    smp_minmax<NT>(mn, 0u, sh.red, &mn, &mx);
     n = ev;
     base = mn;
   } else {
-    // ---- sample: 4 float4 per thread; a wave's load covers one 256-key tile ----
-    uint32_t sk[16];
-    uint32_t mn = 0xFFFFFFFFu, mx = 0;
+    // ---- sample: kSU float4s per thread; a wave's load covers one 256-key tile ----
+    constexpr int kSU = kSmpSample / 4 / NT;
+    uint32_t sk[4 * kSU];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int f = u * kSmpNT + tid, t = f >> 6;
+    for (int u = 0; u < kSU; ++u) {
+      const int f = u * NT + tid, t = f >> 6;
       const int start = int(int64_t(t) * (ev - kSmpTile) / (kSmpTiles - 1)) & ~3;
       const float4 x = s4[(start >> 2) + (f & 63)];
       sk[4 * u] = order_key(x.x);
       sk[4 * u + 1] = order_key(x.y);
       sk[4 * u + 2] = order_key(x.z);
       sk[4 * u + 3] = order_key(x.w);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        mn = min(mn, sk[4 * u + c]);
-        mx = max(mx, sk[4 * u + c]);
-      }
     }
+    // theta = the 22-bit order-key prefix of the sample's r-th largest key: digit 1 is bits 31..21
+    // (in sh.u.hist), digit 2 bits 20..10 among the sample keys of digit 1's bin (in the list's
+    // memory, free until the pass)
+    uint32_t* hist2 = sh.key;
+    zero_words<NT>(sh.u.hist, kSmpBins);
+    zero_words<NT>(hist2, kSmpBins);
     if (tid == 0) sh.n_list = 0;
-    smp_minmax(mn, mx, sh.red, &mn, &mx);
-    const int s1 = max(0, 32 - int(__builtin_clz((mx - mn) | 1u)) - 11);
-    zero_words<kSmpNT>(sh.u.hist, kSmpBins);
     __syncthreads();
 #pragma unroll
-    for (int k = 0; k < 16; ++k) atomicAdd(&sh.u.hist[(sk[k] - mn) >> s1], 1u);
+    for (int k = 0; k < 4 * kSU; ++k) atomicAdd(&sh.u.hist[sk[k] >> 21], 1u);
     __syncthreads();
     // r: smallest rank with r * ev / m - 4 sqrt(r) * ev / m >= K
     const float y = 2.f + sqrtf(4.f + float(K) * float(kSmpSample) / float(ev));
@@ -974,55 +1032,81 @@ __global__ __launch_bounds__(kSmpNT, 5) void topk_sample_kernel(
     if ((tid >> 6) == 0) {
       int bin, rem, cnt;
       wave_select<kSmpBins>(sh.u.hist, r, &bin, &rem, &cnt);
-      if (lane == 0) sh.prefix = mn + (uint32_t(bin) << s1);
+      if (lane == 0) {
+        sh.prefix = uint32_t(bin);
+        sh.remaining = rem;
+      }
+    }
+    __syncthreads();
+    const uint32_t b1 = sh.prefix;
+    const int r2 = sh.remaining;
+#pragma unroll
+    for (int k = 0; k < 4 * kSU; ++k)
+      if ((sk[k] >> 21) == b1) atomicAdd(&hist2[(sk[k] >> 10) & (kSmpBins - 1)], 1u);
+    __syncthreads();
+    if ((tid >> 6) == 0) {
+      int bin, rem, cnt;
+      wave_select<kSmpBins>(hist2, r2, &bin, &rem, &cnt);
+      if (lane == 0) sh.prefix = (b1 << 21) | (uint32_t(bin) << 10);
     }
     __syncthreads();
     base = sh.prefix;  // theta as an order key
-    // ---- one pass: list every key >= theta. A normal theta compares as a float (the same order
-    // for every float, denormals included, -0 == +0); otherwise the order keys are compared. ----
+    // ---- one pass: list every key >= theta (raw float bits and position). The kernels keep f32
+    // denormals (the compiler's default for this library), so the IEEE compare x >= theta orders
+    // every finite score exactly as the order keys do (-0 == +0 in both). ----
     const float theta = key_to_float(base);
-    const bool by_float = fabsf(theta) >= 1.17549435e-38f;
     const int n4 = (ev + 3) >> 2;
-#pragma unroll 1
-    for (int v0 = 0; v0 < n4; v0 += kSmpNT * kSmpU) {
+    constexpr int kSmpU = kSmpInFlight / NT;  // float4 loads in flight per thread (a multiple of 4)
+    static_assert(kSmpU % 4 == 0, "groups of 4 float4s");
+    // one step of NT * kSmpU float4s from v0; FULL: every position of the step is inside the row
+    auto step = [&](auto full_tag, int v0) {
+      constexpr bool FULL = decltype(full_tag)::value;
       float4 x[kSmpU];
 #pragma unroll
       for (int u = 0; u < kSmpU; ++u) {
-        const int q = v0 + u * kSmpNT + tid;
-        x[u] = q < n4 ? s4[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+        const int q = v0 + u * NT + tid;
+        x[u] = (FULL || q < n4) ? s4[q] : make_float4(0.f, 0.f, 0.f, 0.f);
       }
-      const bool full = 4 * (v0 + kSmpNT * kSmpU) <= ev;  // uniform: every position of the step is in the row
-      auto hit = [&](int u, int c) {
-        const float xc = c == 0 ? x[u].x : c == 1 ? x[u].y : c == 2 ? x[u].z : x[u].w;
-        const bool in = full || 4 * (v0 + u * kSmpNT + tid) + c < ev;
-        return in && (by_float ? xc >= theta : order_key(xc) >= base);
-      };
-      uint64_t m[kSmpU][4];
-      int total = 0;
+      // hits are placed in groups of 4 float4s (16 ballots, one LDS slot reservation per group)
 #pragma unroll
-      for (int u = 0; u < kSmpU; ++u)
+      for (int g = 0; g < kSmpU; g += 4) {
+        uint64_t m[4][4];
+        int total = 0;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          m[u][c] = ballot(hit(u, c));
-          total += __popcll(m[u][c]);
-        }
-      if (total == 0) continue;  // uniform per wave
-      int slot = 0;
-      if (lane == 0) slot = atomicAdd(&sh.n_list, total);
-      slot = __builtin_amdgcn_readfirstlane(slot);
+        for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int u = 0; u < kSmpU; ++u)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int sl = slot + lanes_below(m[u][c]);
-          if (((m[u][c] >> lane) & 1ull) && sl < kSmpList) {
-            const float xc = c == 0 ? x[u].x : c == 1 ? x[u].y : c == 2 ? x[u].z : x[u].w;
-            sh.key[sl] = order_key(xc);
-            sh.pos[sl] = uint16_t(4 * (v0 + u * kSmpNT + tid) + c);
+          for (int c = 0; c < 4; ++c) {
+            const float xc = c == 0 ? x[g + u].x : c == 1 ? x[g + u].y : c == 2 ? x[g + u].z : x[g + u].w;
+            const bool in = FULL || 4 * (v0 + (g + u) * NT + tid) + c < ev;
+            m[u][c] = ballot(in && xc >= theta);
+            total += __popcll(m[u][c]);
           }
-          slot += __popcll(m[u][c]);
-        }
-    }
+        if (total == 0) continue;  // uniform per wave
+        int slot = 0;
+        if (lane == 0) slot = atomicAdd(&sh.n_list, total);
+        slot = __builtin_amdgcn_readfirstlane(slot);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int sl = slot + lanes_below(m[u][c]);
+            if (((m[u][c] >> lane) & 1ull) && sl < kSmpList) {
+              const float xc = c == 0 ? x[g + u].x : c == 1 ? x[g + u].y : c == 2 ? x[g + u].z : x[g + u].w;
+              sh.key[sl] = __float_as_uint(xc);
+              sh.pos[sl] = uint16_t(4 * (v0 + (g + u) * NT + tid) + c);
+            }
+            slot += __popcll(m[u][c]);
+          }
+      }
+    };
+    int v0 = 0;
+#pragma unroll 1
+    for (; 4 * (v0 + NT * kSmpU) <= ev; v0 += NT * kSmpU) step(std::true_type{}, v0);
+    if (v0 < n4) step(std::false_type{}, v0);
+    __syncthreads();
+    // raw bits -> order keys, once per listed key
+    const int nl = min(sh.n_list, kSmpList);
+    for (int c = tid; c < nl; c += NT) sh.key[c] = order_key_bits(sh.key[c]);
     __syncthreads();
     n = sh.n_list;
   }
@@ -1376,9 +1460,17 @@ dsa_status launch_topk(const dsa_indexer_topk_args* a, const float* scores, int6
   scores, ld, a->cu_seqlens_q, a->seqused_kv, a->cu_seqlens_kv, a->window_kv_start, a->batch, a->q_stride,     \
       a->compress_ratio, a->nk, max_vis, a->topk, a->window, a->kv_row_base, a->topk_idx, a->err_flag, INT32_MAX
 #define DSA_TOPK_REG(NT, E) hipLaunchKernelGGL((topk_reg_kernel<NT, E>), grid, dim3(NT), 0, stream, DSA_TOPK_ARGS)
-  tap_launch(max_vis <= kSmpMaxRow ? "topk_sample_kernel" : "topk_stream_kernel", stream);
-  if (max_vis <= kSmpMaxRow) hipLaunchKernelGGL(topk_sample_kernel, grid, dim3(kSmpNT), 0, stream, DSA_TOPK_ARGS);
-  else hipLaunchKernelGGL(topk_stream_kernel, grid, dim3(kStreamNT), 0, stream, DSA_TOPK_ARGS);
+  // Launches that fill the GPU about once (at most four rows per CU) are bound by one row's
+  // latency: rows of up to 32768 keys stay in registers, 256 to 1024 threads each. More rows of up
+  // to 32768 keys take the sampled kernel, five per CU; longer rows are streamed.
+  const bool few = a->nq <= 1024;
+  tap_launch(max_vis > kSmpMaxRow ? "topk_stream_kernel" : few ? "topk_reg_kernel" : "topk_sample_kernel", stream);
+  if (max_vis > kSmpMaxRow) hipLaunchKernelGGL(topk_stream_kernel, grid, dim3(kStreamNT), 0, stream, DSA_TOPK_ARGS);
+  else if (!few) hipLaunchKernelGGL(topk_sample_kernel<256>, grid, dim3(256), 0, stream, DSA_TOPK_ARGS);
+  else if (max_vis <= 256 * 16) DSA_TOPK_REG(256, 16);
+  else if (max_vis <= 512 * 16) DSA_TOPK_REG(512, 16);
+  else if (max_vis <= 1024 * 16) DSA_TOPK_REG(1024, 16);
+  else DSA_TOPK_REG(1024, 32);
 #undef DSA_TOPK_REG
 #undef DSA_TOPK_ARGS
   return check_launch("topk_kernel");
