@@ -1460,10 +1460,11 @@ dsa_status launch_topk(const dsa_indexer_topk_args* a, const float* scores, int6
   scores, ld, a->cu_seqlens_q, a->seqused_kv, a->cu_seqlens_kv, a->window_kv_start, a->batch, a->q_stride,     \
       a->compress_ratio, a->nk, max_vis, a->topk, a->window, a->kv_row_base, a->topk_idx, a->err_flag, INT32_MAX
 #define DSA_TOPK_REG(NT, E) hipLaunchKernelGGL((topk_reg_kernel<NT, E>), grid, dim3(NT), 0, stream, DSA_TOPK_ARGS)
-  // Launches that fill the GPU about once (at most four rows per CU) are bound by one row's
-  // latency: rows of up to 32768 keys stay in registers, 256 to 1024 threads each. More rows of up
-  // to 32768 keys take the sampled kernel, five per CU; longer rows are streamed.
-  const bool few = a->nq <= 1024;
+  // Rows of up to 4096 keys stay in registers (256 threads, many rows per CU). Launches that fill
+  // the GPU about once (at most four rows per CU) are bound by one row's latency: rows of up to
+  // 32768 keys stay in registers too, 512 or 1024 threads each. More rows of up to 32768 keys take
+  // the sampled kernel, five per CU; longer rows are streamed.
+  const bool few = a->nq <= 1024 || max_vis <= 256 * 16;
   tap_launch(max_vis > kSmpMaxRow ? "topk_stream_kernel" : few ? "topk_reg_kernel" : "topk_sample_kernel", stream);
   if (max_vis > kSmpMaxRow) hipLaunchKernelGGL(topk_stream_kernel, grid, dim3(kStreamNT), 0, stream, DSA_TOPK_ARGS);
   else if (!few) hipLaunchKernelGGL(topk_sample_kernel<256>, grid, dim3(256), 0, stream, DSA_TOPK_ARGS);

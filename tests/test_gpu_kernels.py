@@ -51,9 +51,9 @@ def _run_topk(scores, m, d, K, dev, ratio=1, window=0, win_start=None, kv_row_ba
     ([9000], 9, 8, 2048),           # 8192 < E <= 9000: 1024 x 16 in registers
     ([20000], 30, 29, 2048),        # E ~ 20000: 1024 x 32 in registers, two workgroups per CU
     ([30000], 200, 199, 2048),      # E ~ 30000: 1024 x 32 in registers
-    # more than 1024 rows: the sampled kernel
-    ([3000], 1, 0, 2048),           # E crosses K; every row is its own list
-    ([6000], 3, 2, 2048),           # 2000 rows, sampled above 3584 keys
+    ([3000], 1, 0, 2048),           # 3000 rows, E crosses K: rows of up to 4096 keys stay in registers
+    # more than 1024 rows of more than 4096 keys: the sampled kernel
+    ([6000], 3, 2, 2048),           # 2000 rows, rows of up to 3584 keys are their own list, longer sampled
     ([9000], 8, 7, 2048),           # 1125 rows of 7876 .. 9000 keys
     ([30000], 16, 15, 2048),        # 1875 rows (more than four per CU): the sampled kernel; rows
                                     # of up to 3584 keys are their own list, longer rows are sampled
