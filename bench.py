@@ -338,6 +338,8 @@ def main():
         print(json.dumps({"error": "graph replay differs from the eager step"}))
         sys.exit(1)
     del graph
+    attn_kernel = "sparse_attn_mla_bf16" if ak == "bf16" and wl.H == 128 else "sparse_attn_generic"
+    ceiling = lds_mfma_ceiling(D, dev) if attn_kernel == "sparse_attn_mla_bf16" and not args.profile_only else None
 
     # ---------------- algorithmic work (per launch) ---------------------------------------------
     m = {k: (v.cpu().numpy() if v is not None else None) for k, v in meta0.items()}
@@ -360,7 +362,6 @@ def main():
     idx_peak = {"bf16": PEAK_BF16_TFLOPS, "fp8": PEAK_FP8_TFLOPS, "f32": PEAK_FP32_TFLOPS}[ik]
     value = n_real / (step_stats["median"] * 1e-3)
 
-    attn_kernel = "sparse_attn_mla_bf16" if ak == "bf16" and wl.H == 128 else "sparse_attn_generic"
     attn_ms = stage_ms["sparse_attn"]["mean"]
     idx_kernel = next((kn for kn in kernel_names if kn.startswith("indexer")), None)
     idx_ms = kernel_mean.get(idx_kernel) if idx_kernel else None
@@ -375,6 +376,12 @@ def main():
         return r
 
     roofs = [roof(attn_kernel, attn_flops, attn_ms, attn_peak)]
+    if ceiling:
+        # what one wave per SIMD can issue, in shader cycles, scaled by the clock the run held
+        c = ceiling["mla_half_tile_1wave"] * float(np.median(mhz)) / 2400.0
+        roofs[0]["lds_mfma_ceiling"] = ceiling
+        roofs[0]["ceiling_frac_of_peak"] = c
+        roofs[0]["frac_of_ceiling"] = roofs[0]["frac"] / c
     if idx_kernel and idx_ms:
         roofs.append(roof(idx_kernel, idx_flops, idx_ms, idx_peak))
     roofs.sort(key=lambda r: -r["avg_launch_ms"])  # the dominant kernel first
@@ -424,6 +431,24 @@ def main():
         print("bench: CPU baseline (oracle sample)", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(wl, inp, qin, args.cpu_seconds)
     print(json.dumps(res), flush=True)
+
+
+def lds_mfma_ceiling(D, dev, iters=200):
+    """MFMA busy fraction one SIMD reaches when its 32x32x16 bf16 MFMAs take their A operand from
+    LDS in the MLA kernel's K form (one 16-byte read) or V form (two transposed 8-byte reads), with
+    one or two waves per SIMD (the library's LDS-fed MFMA probe); mla_half_tile_1wave weighs the
+    two forms as one half-tile of the kernel does (36 logit MFMAs, 32 P.V MFMAs)."""
+    import torch
+    cyc = torch.zeros(2048, dtype=torch.int64, device=dev)
+    sink = torch.empty(256 * 512, dtype=torch.float32, device=dev)
+    out = {}
+    for name, op in (("k_form", 0), ("v_form", 1), ("registers", 2)):
+        for w in (1, 2):
+            D.lds_mfma_probe(op, w, iters, cyc, sink)
+            torch.cuda.synchronize()
+            out[f"{name}_{w}wave"] = round(D.lds_mfma_busy(cyc.cpu().numpy(), w, iters), 4)
+    out["mla_half_tile_1wave"] = round(68.0 / (36.0 / out["k_form_1wave"] + 32.0 / out["v_form_1wave"]), 4)
+    return out
 
 
 def cpu_baseline(wl, inp, qin, budget_s):

@@ -212,6 +212,19 @@ dsa_status dsa_indexer_topk_timed(const dsa_indexer_topk_args* args, void* strea
  * out of range. */
 dsa_status dsa_clock_probe(uint64_t* out, int64_t ticks, void* stream);
 
+/* Measurement hook, for the ceiling of the MLA attention kernel's MFMA rate: enqueues on `stream`
+ * 256 workgroups of 64 * 4 * waves_per_simd threads (one or two waves per SIMD); every wave runs
+ * iters x 32 dependent 32x32x16 bf16 MFMAs whose A operand comes from LDS in the attention
+ * kernel's K form (operand 0: one 16-byte read per lane per MFMA) or V form (operand 1: two 8-byte
+ * transposed reads per lane), or from registers (operand 2), reads issued three MFMAs ahead. Wave w
+ * of workgroup g writes the shader-clock cycles of its loop to cycles[8 g + w] (device, >= 2048
+ * entries; other entries untouched); sink (device, >= 256 x threads floats) receives values that
+ * keep the MFMA chain live. The MFMA busy fraction of a SIMD is 32 x iters x 32 x waves_per_simd
+ * / cycles (32 cycles per MFMA). DSA_ERR_INVALID_ARG for operand outside 0..2, waves_per_simd
+ * outside 1..2, iters outside 1..1e5, or NULL / short buffers. */
+dsa_status dsa_lds_mfma_probe(int32_t operand, int32_t waves_per_simd, int32_t iters, uint64_t* cycles,
+                              int64_t n_cycles, float* sink, int64_t n_sink, void* stream);
+
 /* ------------------------------------------------------------------------------------------
  * (4) Sparse shared-KV (MLA) attention with a per-head sink ([xLLM-CP] Design, data-flow
  * step (4): the local queries of all heads attend over the full KV stream's selected rows and

@@ -66,11 +66,13 @@ def lib():
         L.dsa_topk_from_scores.argtypes = [ctypes.POINTER(IndexerArgs), c_p, c_i64, c_p]
         L.dsa_sparse_attn.argtypes = [ctypes.POINTER(AttnArgs), c_p]
         L.dsa_clock_probe.argtypes = [c_p, c_i64, c_p]
+        L.dsa_lds_mfma_probe.argtypes = [c_i32, c_i32, c_i32, c_p, c_i64, c_p, c_i64, c_p]
         L.dsa_rerange.argtypes = [c_p, c_p, c_i32, c_i64, c_i32, c_i32, c_i32, c_i32, c_p]
         for f in ("dsa_cp_sizes", "dsa_build_cp_metadata", "dsa_indexer_topk", "dsa_indexer_topk_noalloc",
                   "dsa_indexer_topk_timed",
                   "dsa_indexer_scores",
-                  "dsa_topk_from_scores", "dsa_sparse_attn", "dsa_rerange", "dsa_clock_probe"):
+                  "dsa_topk_from_scores", "dsa_sparse_attn", "dsa_rerange", "dsa_clock_probe",
+                  "dsa_lds_mfma_probe"):
             getattr(L, f).restype = c_i32
         _lib = L
     return _lib
@@ -291,6 +293,25 @@ def probe_mhz(out):
     """The shader clock in MHz from a clock_probe result (host copy of its 4 counters)."""
     c0, c1, r0, r1 = (int(x) for x in out[:4])
     return 100.0 * (c1 - c0) / max(r1 - r0, 1)
+
+
+def lds_mfma_probe(operand, waves_per_simd, iters, cycles, sink, stream=None):
+    """Enqueue the LDS-fed MFMA probe (operand 0: K-form reads, 1: V-form transposed reads, 2: none);
+    cycles (int64 GPU tensor, >= 2048) receives per-wave shader-clock cycles at [8 * block + wave],
+    sink (float32 GPU tensor, >= 256 * 256 * waves_per_simd) keeps the MFMA chains live."""
+    _dense("cycles", cycles, (torch.int64,))
+    _dense("sink", sink, torch.float32)
+    _check(lib().dsa_lds_mfma_probe(int(operand), int(waves_per_simd), int(iters), _ptr(cycles), cycles.numel(),
+                                    _ptr(sink), sink.numel(), _stream(stream)), "dsa_lds_mfma_probe")
+    return cycles
+
+
+def lds_mfma_busy(cycles, waves_per_simd, iters):
+    """MFMA busy fraction per SIMD from a lds_mfma_probe result (host array of the 2048 counts):
+    the median over workgroups of the slowest wave's loop."""
+    import numpy as np
+    c = np.asarray(cycles, dtype=np.int64).reshape(256, 8)[:, :4 * waves_per_simd].max(axis=1)
+    return 32.0 * 32 * iters * waves_per_simd / float(np.median(c))
 
 
 def sparse_attn(q, kv, idx, sink, softmax_scale, d_v, out=None, lse=None, err_flag=None, stream=None):

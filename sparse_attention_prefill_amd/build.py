@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libdsa.so")
-SOURCES = ["api.hip", "metadata.hip", "rerange.hip", "indexer.hip", "topk.hip", "attention.hip"]
+SOURCES = ["api.hip", "metadata.hip", "rerange.hip", "indexer.hip", "topk.hip", "attention.hip", "probes.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -40,7 +40,7 @@ def _compile(src):
 
 def build_library(verbose=False):
     os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(len(SOURCES), 6)) as ex:
+    with ThreadPoolExecutor(max_workers=min(len(SOURCES), 7)) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs

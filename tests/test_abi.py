@@ -138,3 +138,17 @@ def test_timed_indexer_rejects_missing_events_before_launch():
     ev = (ctypes.c_void_p * 3)(16, None, 32)
     assert L.dsa_indexer_topk_timed(ctypes.byref(g), None, ev, 3, ctypes.byref(n), None) == 1
     assert b"NULL event" in L.dsa_last_error() and n.value == -1
+
+
+def test_measurement_probes_reject_bad_arguments_before_launch():
+    import sparse_attention_prefill_amd as D
+    L = D.lib()
+    assert L.dsa_clock_probe(None, 100, None) == 1
+    assert L.dsa_clock_probe(ctypes.c_void_p(256), 0, None) == 1
+    p = ctypes.c_void_p(256)
+    assert L.dsa_lds_mfma_probe(3, 1, 10, p, 2048, p, 65536, None) == 1       # operand
+    assert L.dsa_lds_mfma_probe(0, 3, 10, p, 2048, p, 65536, None) == 1       # waves per SIMD
+    assert L.dsa_lds_mfma_probe(0, 1, 0, p, 2048, p, 65536, None) == 1        # iterations
+    assert L.dsa_lds_mfma_probe(1, 1, 10, p, 2047, p, 65536, None) == 1       # short cycle buffer
+    assert L.dsa_lds_mfma_probe(1, 2, 10, p, 2048, p, 65536, None) == 1       # sink for 512 threads
+    assert b"sink" in L.dsa_last_error()
