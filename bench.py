@@ -29,6 +29,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -106,6 +107,23 @@ def settle(run, ms):
     return n
 
 
+def short_kernel_name(name):
+    """A profiler's demangled kernel name without return type, namespaces and argument list:
+    'void dsa::(anonymous namespace)::indexer_mfma<true, true>(unsigned char const*, ...)' ->
+    'indexer_mfma<true, true>'."""
+    name = re.sub(r"^void ", "", name)
+    name = re.sub(r"^dsa::\(anonymous namespace\)::", "", name)
+    depth = 0
+    for i, ch in enumerate(name):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            return name[:i]
+    return name
+
+
 def summarize_counters(args):
     """profiles/traffic_<kernel>_<workload>.json from rocprofv3 --pmc CSV output directories."""
     def per_dispatch(d, counter, trace_name):
@@ -114,7 +132,7 @@ def summarize_counters(args):
             for row in csv.DictReader(open(f)):
                 if row.get("Counter_Name") != counter:
                     continue
-                name = row.get("Kernel_Name", "")
+                name = short_kernel_name(row.get("Kernel_Name", ""))
                 if trace_name is not None and not name.startswith(trace_name):
                     continue
                 key = (f, row.get("Dispatch_Id"))

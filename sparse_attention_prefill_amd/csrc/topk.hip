@@ -23,6 +23,9 @@
 // is selected exactly, and the ids are emitted from LDS bitmaps. When the list ends up with
 // fewer than K keys or overflows, the row falls back to an exact histogram over the whole row
 // (then keys above b* go straight to the bitmaps and only b*'s keys are listed).
+// Launches of more than 1024 rows of 4097 .. 32768 keys take topk_sample_kernel: the same
+// sample / list / exact-select scheme in 256 threads and about 32 KB of LDS per row, so five
+// rows share a CU (its section below).
 #include "index_score.h"
 
 namespace dsa {
