@@ -423,8 +423,9 @@ def main():
                    "window": wl.window, "compress": wl.compress},
         "roofline": roofs[0],
         "roofline_secondary": roofs[1] if len(roofs) > 1 else None,
-        "mfma_util": {"path_bf16_peak_frac": (attn_flops + idx_flops) / (step_stats["median"] * 1e-3) / 1e12
-                      / PEAK_BF16_TFLOPS,
+        # time the step's MFMA work would take at each kernel's own dtype peak, over the step time
+        "mfma_util": {"path_peak_frac": (attn_flops / (attn_peak * 1e12) + idx_flops / (idx_peak * 1e12))
+                      / (step_stats["median"] * 1e-3),
                       "sparse_attn_frac": roofs[[r["kernel"] for r in roofs].index(attn_kernel)]["frac"],
                       "indexer_frac": (idx_flops / (idx_ms * 1e-3) / 1e12 / idx_peak) if idx_ms else None},
         "stages_ms": stage_ms,
