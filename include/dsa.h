@@ -22,6 +22,11 @@
  *     only visible on the device (e.g. cu-seqlens that do not match the row count) are reported
  *     by OR-ing DSA_DEVERR_* bits into *err_flag (device int32, optional) and the offending row
  *     is skipped, so nothing is read out of bounds.
+ *   - Checked build: libdsa_checked.so (the same sources compiled with DSA_CHECKED) also verifies,
+ *     before each use, every gathered KV / key row id and every data-dependent LDS or output index
+ *     the kernels compute (list slots, compacted-row slots, histogram bins, bitmap words, output
+ *     positions). A failed check ORs DSA_DEVERR_BOUNDS into *err_flag and skips that access; no
+ *     check traps. Its results are those of libdsa.so bit for bit; it is for testing, not speed.
  *   - The library is reentrant; its only state is the per-thread error string.
  */
 #ifndef DSA_H
@@ -61,6 +66,7 @@ typedef enum {
 #define DSA_DEVERR_ROWS 0x10          /* local cu_seqlens_q[B] != nq (global metadata passed?)   */
 #define DSA_DEVERR_EXTENT 0x20        /* a query's causal extent is outside the key buffer       */
 #define DSA_DEVERR_INDEX 0x40         /* a selected KV row id is outside [-1, n_rows)            */
+#define DSA_DEVERR_BOUNDS 0x80        /* checked build only: an internal index failed its check  */
 
 /* Message describing the last error returned on the calling thread ("" if none). */
 const char* dsa_last_error(void);

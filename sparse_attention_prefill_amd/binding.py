@@ -5,6 +5,7 @@ given. Every call raises DsaError with the library's message when the C call fai
 bf16 tensors are torch.bfloat16; fp8 E4M3FN tensors are torch.uint8 (raw bytes) or
 torch.float8_e4m3fn.
 """
+import contextlib
 import ctypes
 import os
 
@@ -12,6 +13,8 @@ import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(HERE, "libdsa.so")
+# the same sources built with DSA_CHECKED: bounds-checked indices, failures in err_flag (tests only)
+checked_library_path = os.path.join(HERE, "libdsa_checked.so")
 
 DSA_F32, DSA_BF16, DSA_FP8_E4M3 = 0, 1, 2
 IN_SEQ, ROUND_ROBIN = 0, 1
@@ -43,6 +46,19 @@ class AttnArgs(ctypes.Structure):
 
 
 _lib = None
+
+
+@contextlib.contextmanager
+def library(path):
+    """Route the calls made inside the block to the library at `path` (e.g. checked_library_path);
+    the previous library is used again afterwards. Not for concurrent use from several threads."""
+    global _lib, library_path
+    saved = (_lib, library_path)
+    _lib, library_path = None, path
+    try:
+        yield lib()
+    finally:
+        _lib, library_path = saved
 
 
 def lib():

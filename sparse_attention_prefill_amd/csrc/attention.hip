@@ -135,7 +135,7 @@ __global__ __launch_bounds__(kGenThreads) void sparse_attn_generic(
         if (e < n) {
           const int rr = e / c4, c = e - rr * c4;
           const int r = srow[rr];
-          if (r >= 0) x[k] = load_elt4(kv, int64_t(r) * Dqk + 4 * c);
+          if (r >= 0 && DSA_CHECK(r < n_rows, err_flag)) x[k] = load_elt4(kv, int64_t(r) * Dqk + 4 * c);
         }
       }
 #pragma unroll
@@ -150,7 +150,7 @@ __global__ __launch_bounds__(kGenThreads) void sparse_attn_generic(
       for (int e = tid; e < kGenTile * P; e += kGenThreads) {
         const int rr = e / P, d = e - rr * P;
         const int r = srow[rr];
-        skv[e] = r >= 0 && d < Dqk ? load_elt(kv, int64_t(r) * Dqk + d) : 0.f;
+        skv[e] = r >= 0 && d < Dqk && DSA_CHECK(r < n_rows, err_flag) ? load_elt(kv, int64_t(r) * Dqk + d) : 0.f;
       }
     }
     __syncthreads();
@@ -342,11 +342,12 @@ __device__ inline int compact_rows(int (&vals)[kSelPer], int n_rows, int tile, i
   int pos = base + incl - cnt;
 #pragma unroll
   for (int k = 0; k < kPer; ++k)
-    if (vals[k] >= 0) rows[pos++] = vals[k];
+    if (vals[k] >= 0 && DSA_CHECK(pos < kMaxKtot, err_flag)) rows[pos++] = vals[k];
   __syncthreads();
   const int n_sel = scan[kWaves];
   const int padded = (n_sel + tile - 1) / tile * tile;
-  for (int e = n_sel + tid; e < padded; e += kThreads) rows[e] = 0;
+  for (int e = n_sel + tid; e < padded; e += kThreads)
+    if (DSA_CHECK(e < kMaxKtot, err_flag)) rows[e] = 0;
   __syncthreads();
   return n_sel;
 }
@@ -408,6 +409,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
     int lat, rope0, rope1;
   };
   auto gather_rows = [&](int t) {
+    if (!DSA_CHECK((t + 1) * kTile <= kMaxKtot, err_flag)) return GatherRows{0, 0, 0};
     return GatherRows{rows[t * kTile + 16 * wave + (lane & 15)], rows[t * kTile + 16 * wave + (lane >> 3)],
                       rows[t * kTile + 16 * wave + 8 + (lane >> 3)]};
   };
@@ -417,12 +419,14 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_mla_bf16(
     const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_offset(tiles + buf * kTileBytes));
     if (j < 16) {
       const int r = __builtin_amdgcn_readlane(gr.lat, j);
-      lds_dma16_s(kvb + int64_t(r) * kRowBytes, lane16, dst + uint32_t((16 * wave + j) * kLatPitch));
+      if (DSA_CHECK(r >= 0 && r < n_rows, err_flag))
+        lds_dma16_s(kvb + int64_t(r) * kRowBytes, lane16, dst + uint32_t((16 * wave + j) * kLatPitch));
     } else {
       const int n0 = 16 * wave + 8 * (j - 16);  // rows n0 + lane/8
       const int c = (lane & 7) ^ rope_swz(n0 + (lane >> 3));
-      lds_dma16_v(kvb + int64_t(j == 16 ? gr.rope0 : gr.rope1) * kRowBytes + kLatBytes + (c << 4),
-                  dst + uint32_t(kLatTile + n0 * kRopeBytes));
+      const int r = j == 16 ? gr.rope0 : gr.rope1;
+      if (DSA_CHECK(r >= 0 && r < n_rows, err_flag))
+        lds_dma16_v(kvb + int64_t(r) * kRowBytes + kLatBytes + (c << 4), dst + uint32_t(kLatTile + n0 * kRopeBytes));
     }
   };
   auto issue_tile = [&](int t, int buf) {

@@ -77,6 +77,16 @@ __device__ inline void raise_flag(int32_t* err_flag, int32_t bits) {
   if (err_flag) atomicOr(err_flag, bits);
 }
 
+// Checked build (DSA_CHECKED): DSA_CHECK(cond, err_flag) is false, after OR-ing
+// DSA_DEVERR_BOUNDS into *err_flag, when cond fails; the caller then skips the access. In the
+// product build it is the constant true and the condition is not evaluated.
+#ifdef DSA_CHECKED
+#define DSA_CHECK(cond, err_flag) \
+  (__builtin_expect(!!(cond), 1) ? true : (raise_flag((err_flag), DSA_DEVERR_BOUNDS), false))
+#else
+#define DSA_CHECK(cond, err_flag) true
+#endif
+
 // Causal view of local query row i: request b, extent E (keys seen), key offset kv0.
 // Returns false (and flags) when the row is not covered by the local cu-seqlens.
 struct QueryView {

@@ -72,7 +72,7 @@ __global__ __launch_bounds__(kGenThreads) void indexer_generic(
   for (int e = threadIdx.x; e < H; e += kGenThreads) sq[H * D + e] = w[int64_t(i) * H + e];
   __syncthreads();
   const int s = blockIdx.x * kGenThreads + threadIdx.x;
-  if (s >= ev) return;
+  if (s >= ev || !DSA_CHECK(s < ld, err_flag)) return;
   const int64_t krow = int64_t(v.kv0 + s) * D;
   float acc = 0.f;
   if constexpr (KD > 0) {
@@ -214,7 +214,7 @@ __global__ __launch_bounds__(kThreads, FP8 ? 4 : 1) void indexer_mfma(
         int row = glo + t * kKeyTile + n;
         row = row < nk ? row : nk - 1;
         const unsigned char* src = ki + int64_t(row) * C::kKeyBytes + c * 16;
-        lds_dma16_v(src, __builtin_amdgcn_readfirstlane(lds_offset(dst + f0 * 16)));
+        if (DSA_CHECK(row >= 0, err_flag)) lds_dma16_v(src, __builtin_amdgcn_readfirstlane(lds_offset(dst + f0 * 16)));
       }
     };
 
@@ -225,8 +225,9 @@ __global__ __launch_bounds__(kThreads, FP8 ? 4 : 1) void indexer_mfma(
         constexpr int kPerWave = kKeyTile / kWaves;  // scales each wave stages
         if (lane < kPerWave) {
           const int key = glo + t * kKeyTile + kPerWave * wave + lane;
-          lds_dma4_v(k_scale + (key < nk ? key : nk - 1),
-                     __builtin_amdgcn_readfirstlane(lds_offset(ks_tile[buf] + kPerWave * wave)));
+          if (DSA_CHECK(key >= 0, err_flag))
+            lds_dma4_v(k_scale + (key < nk ? key : nk - 1),
+                       __builtin_amdgcn_readfirstlane(lds_offset(ks_tile[buf] + kPerWave * wave)));
         }
       }
     };
@@ -262,10 +263,11 @@ __global__ __launch_bounds__(kThreads, FP8 ? 4 : 1) void indexer_mfma(
             const uint64_t m = ballot(hit);
             if (m) {
               const int slot = st_n + lanes_below(m);
-              if (hit && slot < seg_cap) seg[slot] = make_uint2(__float_as_uint(sacc), uint32_t(key - q_origin));
+              if (hit && slot < seg_cap && DSA_CHECK(key >= q_origin, err_flag))
+                seg[slot] = make_uint2(__float_as_uint(sacc), uint32_t(key - q_origin));
               st_n += __popcll(m);
             }
-          } else if (in) {
+          } else if (in && DSA_CHECK(key >= q_origin && key - q_origin < ld, err_flag)) {
             if constexpr (FP8) sacc *= ks_tile[buf][32 * nb + l32];
             scores[int64_t(i) * ld + (key - q_origin)] = sacc + 0.f;  // -0.0 -> +0.0
           }

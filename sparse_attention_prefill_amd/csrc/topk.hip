@@ -426,7 +426,8 @@ __global__ __launch_bounds__(NT, NT == 1024 ? 8 : 1) void topk_reg_kernel(
       const uint32_t pj = __builtin_amdgcn_readlane(pref, j);
       const bool sel = keys[j] >= tau;
       const uint64_t s = ballot(sel);
-      if (sel) orow[int(pj & 0xFFFFu) + int(pj >> 16) + lanes_below(s)] = ri.base + j * NT + tid;
+      if (sel && DSA_CHECK(int(pj & 0xFFFFu) + int(pj >> 16) + lanes_below(s) < K, err_flag))
+        orow[int(pj & 0xFFFFu) + int(pj >> 16) + lanes_below(s)] = ri.base + j * NT + tid;
     });
   } else {  // ties at tau beyond the quota: the lowest positions win
     for_chunks([&](int j) {
@@ -436,7 +437,8 @@ __global__ __launch_bounds__(NT, NT == 1024 ? 8 : 1) void topk_reg_kernel(
       const uint64_t e = ballot(is_eq);
       const bool sel = keys[j] > tau || (is_eq && eq_before + lanes_below(e) < need);
       const uint64_t s = ballot(sel);
-      if (sel) orow[gt_before + min(eq_before, need) + lanes_below(s)] = ri.base + j * NT + tid;
+      if (sel && DSA_CHECK(gt_before + min(eq_before, need) + lanes_below(s) < K, err_flag))
+        orow[gt_before + min(eq_before, need) + lanes_below(s)] = ri.base + j * NT + tid;
     });
   }
   const int n_sel = int(tot & 0xFFFFu) + (take_all ? int(tot >> 16) : min(int(tot >> 16), need));
@@ -1349,7 +1351,7 @@ __global__ __launch_bounds__(kCandNT, 2) void topk_cand_kernel(
     const int c = j * NT + tid, y = c / seg_cap;
     const bool valid = y < segs && c - y * seg_cap < sh.seg_n[min(y, segs - 1)];
     const uint2 e = valid ? crow[c] : uint2{0u, 0u};
-    pos[j] = valid ? int(e.y) : -1;
+    pos[j] = valid && DSA_CHECK(e.y < uint32_t(ev), err_flag) ? int(e.y) : -1;  // list positions index the bitmaps
     d[j] = valid ? order_key_bits(e.x) - th : 0u;
     mx = max(mx, d[j]);
   }

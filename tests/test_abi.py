@@ -152,3 +152,12 @@ def test_measurement_probes_reject_bad_arguments_before_launch():
     assert L.dsa_lds_mfma_probe(1, 1, 10, p, 2047, p, 65536, None) == 1       # short cycle buffer
     assert L.dsa_lds_mfma_probe(1, 2, 10, p, 2048, p, 65536, None) == 1       # sink for 512 threads
     assert b"sink" in L.dsa_last_error()
+
+
+def test_checked_library_exports_every_declared_symbol():
+    import sparse_attention_prefill_amd as D
+    with D.library(D.checked_library_path) as L:
+        missing = [n for n in declared_functions() if not hasattr(L, n)]
+        assert not missing, missing
+        assert L.dsa_sparse_attn(None, None) == 1      # the same host checks
+    assert D.lib()._name == D.library_path
