@@ -3,7 +3,8 @@
 //
 // [xLLM-CP] "feat: DeepSeek-V4 DSA context-parallel on NPU", Design, data-flow step (3):
 //   score(i, s) = sum_h w[i,h] * max(0, q_idx[i,h,:] . k_idx[s,:])   (64 heads x 128)
-// fp8 (E4M3): q_scale[i,h] is folded into the weight and k_scale[s] multiplies the head sum.
+// fp8 (E4M3): q_scale[i,h] is folded into the weight and k_scale[s] multiplies the head sum, which
+// fp8 computes through ReLU(x) = (x + |x|) / 2 (see "fp8: the score through ..." below).
 //
 // Layout: one wave owns one query. A 32-key block takes two 32x32 MFMA chains (heads 0..31 and
 // 32..63) over the 128 dimensions; lane l holds key 32*nb + (l & 31) and, in each chain, heads
@@ -98,6 +99,103 @@ __device__ inline float block_head_sum(const float (&wv)[2][16], const f32x16& a
   return xor32_sum(sacc);
 }
 
+// ---- fp8: the score through ReLU(x) = (x + |x|) / 2 ----
+// With w''_h = w_h q_scale_h / 2 and x_h = q_h . k (the fp8 dot product of the matrix cores),
+//   sum_h w_h q_scale_h ReLU(x_h) = sum_h w''_h |x_h| + c . k,   c_d = sum_h w''_h q_hd,
+// an identity, not an approximation. The first sum costs one FMA per head (|x| is a free source
+// modifier of the FMA) where the ReLU form costs a max and an FMA; the second is one dot product
+// per key, computed on the matrix cores from c split into kLinParts fp8 parts:
+//   c_d = 2^e0 * sum_p 16^-p P_pd + r_d,   2^(e0 + 7) <= max_d |c_d| < 2^(e0 + 8),
+//   |r_d| <= 2^(e0 - 9) <= 2^-16 max_d |c_d|.
+// Every split step is exact: P_pd is the running remainder (in units of 2^e0 16^-p, below 256 in
+// magnitude) rounded to E4M3 (round to nearest even, so within 8 units), remainder - P_pd is exact
+// in fp32 (Sterbenz: the two are within a factor of two, or P_pd is 0), and the scaling by 16 that
+// gives the next remainder (below 128) is exact. fp8 scores of every kernel go through lin_split /
+// lin_combine / block_abs_sum in this order, so a (query, key) score is the same float whichever
+// kernel computed it.
+constexpr int kLinParts = 4;
+
+// The four dimensions 4 (lane & 31) .. +3 of c for query i, in both halves of the wave, split into
+// fp8 parts: part[p] holds P_p of those dimensions (byte k = dimension 4 (lane & 31) + k). wv are
+// the halved weights w'' in output layout (load_query_operands, then * 0.5). Returns e0.
+__device__ inline int lin_split(const unsigned char* __restrict__ qi, const float (&wv)[2][16], int i,
+                                uint32_t (&part)[kLinParts]) {
+  const int lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
+  const unsigned char* qrow = qi + int64_t(i) * kIdxHeads * kIdxDim + 4 * l32;
+  float c[4] = {0.f, 0.f, 0.f, 0.f};
+  // half h sums the 32 heads it holds in output layout (head bit 2 == h); the halves then add
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int hh = 32 * m + 8 * (r >> 2) + 4 * half + (r & 3);
+      const int x = *reinterpret_cast<const int*>(qrow + hh * kIdxDim);
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(x, false), hi = __builtin_amdgcn_cvt_pk_f32_fp8(x, true);
+      c[0] = fmaf(wv[m][r], lo[0], c[0]);
+      c[1] = fmaf(wv[m][r], lo[1], c[1]);
+      c[2] = fmaf(wv[m][r], hi[0], c[2]);
+      c[3] = fmaf(wv[m][r], hi[1], c[3]);
+    }
+  }
+  float mx = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    c[k] = xor32_sum(c[k]);
+    mx = fmaxf(mx, fabsf(c[k]));
+  }
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  // 2^(e0 + 7) <= max |c| < 2^(e0 + 8): the leading part spans [128, 256) at most; the clamp keeps
+  // every part scale a normal float (an all-zero c takes e0 = 0)
+  const int e_max = int((__float_as_uint(mx) >> 23) & 255u) - 127;
+  const int e0 = mx > 0.f ? min(max(e_max - 7, -110), 120) : 0;
+  float r[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) r[k] = ldexpf(c[k], -e0);
+#pragma unroll
+  for (int p = 0; p < kLinParts; ++p) {
+    int wd = __builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[1], 0, false);
+    wd = __builtin_amdgcn_cvt_pk_fp8_f32(r[2], r[3], wd, true);
+    part[p] = uint32_t(wd);
+    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(wd, false), hi = __builtin_amdgcn_cvt_pk_f32_fp8(wd, true);
+    r[0] = (r[0] - lo[0]) * 16.f;
+    r[1] = (r[1] - lo[1]) * 16.f;
+    r[2] = (r[2] - hi[0]) * 16.f;
+    r[3] = (r[3] - hi[1]) * 16.f;
+  }
+  return e0;
+}
+
+// A operand of k-step ks for output row `row` from part rows of 128 fp8 bytes in LDS, stored with
+// the key tiles' chunk swizzle (lin_row_store), so that the 32 rows read together hit distinct
+// banks: the row's dimensions 64ks + 32(lane/32) .. +32
+__device__ inline i32x8 lin_a_operand(const unsigned char* rows, int row, int ks,
+                                       int half = (threadIdx.x & 63) >> 5);
+
+// c . k of one query from its parts' products L[b + p] (the matrix cores' P_p . k), times k's
+// scale. The result is pinned where it is computed: a value used only under a lane condition could
+// otherwise have its MFMAs moved into that branch, where the inactive lanes' operand halves drop
+// out of the products.
+__device__ inline float lin_combine(const f32x16& L, int b, int e0, float k_scale) {
+  float s = fmaf(L[b + 3], 0.0625f, L[b + 2]);
+  s = fmaf(s, 0.0625f, L[b + 1]);
+  s = fmaf(s, 0.0625f, L[b]);
+  float r = ldexpf(s, e0) * k_scale;
+  asm volatile("" : "+v"(r));
+  return r;
+}
+
+// sum over the 64 heads of w'' * |q . k| for the lane's key (both halves hold the result)
+__device__ inline float block_abs_sum(const float (&wv)[2][16], const f32x16& a0, const f32x16& a1) {
+  float sacc = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    sacc = fmaf(wv[0][r], fabsf(a0[r]), sacc);
+    sacc = fmaf(wv[1][r], fabsf(a1[r]), sacc);
+  }
+  return xor32_sum(sacc);
+}
+
 // B operand of k-step ks read straight from key row `row` in global memory
 template <bool FP8>
 __device__ inline typename IdxOps<FP8>::AOp key_operand_global(const unsigned char* __restrict__ ki, int row, int ks) {
@@ -124,9 +222,9 @@ __device__ inline int kswz(int n, int c) {
 
 // B operand of k-step ks for key row n of an LDS tile laid out with kswz
 template <bool FP8>
-__device__ inline typename IdxOps<FP8>::AOp key_operand_lds(const unsigned char* tb, int n, int ks) {
+__device__ inline typename IdxOps<FP8>::AOp key_operand_lds(const unsigned char* tb, int n, int ks,
+                                                            int half = (threadIdx.x & 63) >> 5) {
   constexpr int kBytes = IdxOps<FP8>::kKeyBytes, kChunks = kBytes / 16;
-  const int half = (threadIdx.x & 63) >> 5;
   if constexpr (FP8) {
     const int c0 = 4 * ks + 2 * half;  // two 16-byte chunks: d in [64ks + 32half, +32)
     const i32x4 x0 = *reinterpret_cast<const i32x4*>(tb + n * kBytes + kswz<kChunks>(n, c0) * 16);
@@ -137,17 +235,44 @@ __device__ inline typename IdxOps<FP8>::AOp key_operand_lds(const unsigned char*
   }
 }
 
+// Store dword `word` (dimensions 4c .. 4c + 3) of part row `row` in the swizzled layout
+__device__ inline void lin_row_store(unsigned char* rows, int row, int c, uint32_t word) {
+  *reinterpret_cast<uint32_t*>(rows + row * kIdxDim + kswz<kIdxDim / 16>(row, c >> 2) * 16 + 4 * (c & 3)) = word;
+}
+__device__ inline i32x8 lin_a_operand(const unsigned char* rows, int row, int ks, int half) {
+  const int c0 = 4 * ks + 2 * half;
+  const i32x4 x0 = *reinterpret_cast<const i32x4*>(rows + row * kIdxDim + kswz<kIdxDim / 16>(row, c0) * 16);
+  const i32x4 x1 = *reinterpret_cast<const i32x4*>(rows + row * kIdxDim + kswz<kIdxDim / 16>(row, c0 + 1) * 16);
+  return i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+}
+
 // Full score of key row `row` for the lane (every lane of the wave computes its own key; the
-// 32 lanes of each half must name the same 32 keys, lanes l and l + 32 the same key)
+// 32 lanes of each half must name the same 32 keys, lanes l and l + 32 the same key). fp8: wv are
+// the halved weights, lin_rows this query's kLinParts part rows (128 bytes each, in LDS) and e0
+// its scale exponent (lin_split).
 template <bool FP8>
 __device__ inline float key_score_global(const typename IdxOps<FP8>::AOp (&qa)[2][IdxOps<FP8>::kKsteps],
-                                         const float (&wv)[2][16], const unsigned char* __restrict__ ki,
-                                         const float* __restrict__ k_scale, int row) {
+                                         const float (&wv)[2][16], const unsigned char* lin_rows, int e0,
+                                         const unsigned char* __restrict__ ki, const float* __restrict__ k_scale,
+                                         int row) {
   f32x16 a0, a1;
-  block_mfma_chains<FP8>(qa, [&](int ks) { return key_operand_global<FP8>(ki, row, ks); }, a0, a1);
-  float s = block_head_sum(wv, a0, a1);
-  if constexpr (FP8) s *= k_scale[row];
-  return s + 0.f;  // -0.0 -> +0.0
+  if constexpr (FP8) {
+    // the linear part first (its accumulators are dead before the head chains start); output
+    // rows 8j + 4h + p all read part p, so L[p] is P_p . k in both halves
+    f32x16 L = f32x16{};
+    const int l32 = threadIdx.x & 31;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      L = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(lin_a_operand(lin_rows, l32 & (kLinParts - 1), ks),
+                                                          key_operand_global<true>(ki, row, ks), L, 0, 0, 0, 127, 0, 127);
+    const float ks_row = k_scale[row];
+    const float lin = lin_combine(L, 0, e0, ks_row);
+    block_mfma_chains<FP8>(qa, [&](int ks) { return key_operand_global<FP8>(ki, row, ks); }, a0, a1);
+    return fmaf(block_abs_sum(wv, a0, a1), ks_row, lin) + 0.f;  // -0.0 -> +0.0
+  } else {
+    block_mfma_chains<FP8>(qa, [&](int ks) { return key_operand_global<FP8>(ki, row, ks); }, a0, a1);
+    return block_head_sum(wv, a0, a1) + 0.f;
+  }
 }
 
 }  // namespace dsa

@@ -102,6 +102,21 @@ __global__ __launch_bounds__(kGenThreads) void indexer_generic(
   scores[int64_t(i) * ld + s] = acc + 0.f;  // -0.0 -> +0.0
 }
 
+// A wave-uniform pointer, in scalar registers whatever the compiler could prove about it.
+__device__ inline const void* uniform_ptr(const void* p) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(u));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(u >> 32));
+  return reinterpret_cast<const void*>((uint64_t(hi) << 32) | lo);
+}
+// Direct global->LDS 4-byte loads from a uniform base and a per-lane byte offset: lane l's word
+// lands at lds_base + 4*l (M0 is written only here and in the other direct-load helpers).
+__device__ inline void lds_dma4_s(const void* gbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(uniform_ptr(gbase)),
+               "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory", "m0");
+}
+
 // ---------------------------------------------------------------------------------------------
 // MFMA kernel: 64 heads x 128
 // ---------------------------------------------------------------------------------------------
@@ -111,6 +126,9 @@ constexpr int kWaves = 8, kThreads = kWaves * 64;
 constexpr int kKeyTile = 256;     // keys per LDS tile (one barrier per tile)
 constexpr int kChunkKeys = 4096;  // smallest key chunk per workgroup (grid.y splits longer ranges)
 constexpr int kTargetWorkgroups = 4096;    // chunks grow until the grid is about this large
+// fp8: row pitch (floats) of the per-query linear parts of a tile; the two lane halves write rows
+// q and q + 1 at once, 32 banks apart
+constexpr int kLinPitch = kKeyTile + 32;
 
 template <bool FP8>
 struct IdxCfg {
@@ -138,7 +156,11 @@ __global__ __launch_bounds__(kThreads, FP8 ? 4 : 1) void indexer_mfma(
   using C = IdxCfg<FP8>;
   __shared__ __attribute__((aligned(16))) unsigned char tiles[2 * C::kTileBytes];
   __shared__ __attribute__((aligned(16))) float ks_tile[2][FP8 ? kKeyTile : 4];
-  __shared__ int s_lo[kWaves], s_hi[kWaves];
+  // fp8: the group's split c rows (row 8j + 4h + p: part p of query 2j + h) and each tile's linear
+  // parts c . k times k_scale, [query][key of the tile]
+  __shared__ __attribute__((aligned(16))) unsigned char lin_rows[FP8 ? 32 * kDi : 16];
+  __shared__ __attribute__((aligned(16))) float lin_v[FP8 ? kWaves * kLinPitch : 4];
+  __shared__ int s_lo[kWaves], s_hi[kWaves], s_e0[kWaves];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave (known to the compiler)
@@ -172,6 +194,9 @@ __global__ __launch_bounds__(kThreads, FP8 ? 4 : 1) void indexer_mfma(
     ulo = min(ulo, s_lo[k]);
     uhi = max(uhi, s_hi[k]);
   }
+  // the same in every lane; scalar, so that the tile addresses derived from them are too
+  ulo = __builtin_amdgcn_readfirstlane(ulo);
+  uhi = __builtin_amdgcn_readfirstlane(uhi);
   // The union is cut into chunks of chunk_keys keys; workgroup y takes chunks y, y + gridDim.y,
   // ... A union can be longer than the longest single range (queries of two requests), so the
   // grid-stride loop, not the grid size, guarantees that every chunk is covered.
@@ -182,6 +207,22 @@ __global__ __launch_bounds__(kThreads, FP8 ? 4 : 1) void indexer_mfma(
   typename IdxOps<FP8>::AOp qa[2][kKsteps];
   float wv[2][16];  // weights of the 16 heads this lane holds per head block, in output layout
   if (ok) load_query_operands<FP8>(qi, w, q_scale, i, qa, wv);
+  if constexpr (FP8) {
+    // score = sum_h w'' |x_h| + c . k with w'' = w q_scale / 2 (exact halving); this wave splits
+    // its query's c and stores the parts as rows of the group's c-row operand
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) wv[m][r] *= 0.5f;
+    uint32_t part[kLinParts] = {0u, 0u, 0u, 0u};
+    const int e0 = ok && hi > lo ? lin_split(qi, wv, i, part) : 0;
+    if (half == 0) {
+#pragma unroll
+      for (int p = 0; p < kLinParts; ++p)
+        lin_row_store(lin_rows, 8 * (wave >> 1) + 4 * (wave & 1) + p, l32, part[p]);
+    }
+    if (lane == 0) s_e0[wave] = e0;
+  }
 
   // Candidate mode: this wave's row keeps the scores whose order key is >= theta_k, appended to
   // its own segment of the row's list (segment blockIdx.y of gridDim.y, seg_cap entries) with a
@@ -201,20 +242,29 @@ __global__ __launch_bounds__(kThreads, FP8 ? 4 : 1) void indexer_mfma(
     const int ghi = int(min(int64_t(uhi), int64_t(glo) + chunk_keys));
     const int lo_c = max(lo, glo), hi_c = min(hi, ghi);
     const int n_tiles = (ghi - glo + kKeyTile - 1) / kKeyTile;
-    // ---- staging: tile t holds keys glo + 128t + [0, 128); lane loads 16-byte chunks ----
+    // ---- staging: tile t holds keys glo + 256t + [0, 256); lane loads 16-byte chunks ----
+    // Addresses are a wave-uniform base (scalar registers) plus a 32-bit lane offset, which keeps
+    // the per-lane part to one register per load. Rows past the key buffer read its last row (the
+    // tile may run past the chunk's end).
     auto issue_tile = [&](int t, int buf) {
       unsigned char* dst = tiles + buf * C::kTileBytes;
+      const int row0 = glo + t * kKeyTile;  // < nk: every range ends inside the key buffer
+      const int last = nk - 1 - row0;
+      const unsigned char* gbase = ki + int64_t(row0) * C::kKeyBytes;
+      // fp8 score rows: recomputed from an opaque copy of the lane id (the score-row epilogue
+      // leaves no registers to keep these offsets in; see the tile loop)
+      int ln = lane;
+      if constexpr (FP8 && !CAND) asm volatile("" : "+v"(ln));
 #pragma unroll
       for (int j = 0; j < C::kLoads; ++j) {
         const int f0 = 64 * (C::kLoads * wave + j);
-        const int f = f0 + lane;
+        const int f = f0 + ln;
         const int n = f / C::kChunks;
         const int cp = f - n * C::kChunks;
         const int c = kswz<C::kChunks>(n, cp);
-        int row = glo + t * kKeyTile + n;
-        row = row < nk ? row : nk - 1;
-        const unsigned char* src = ki + int64_t(row) * C::kKeyBytes + c * 16;
-        if (DSA_CHECK(row >= 0, err_flag)) lds_dma16_v(src, __builtin_amdgcn_readfirstlane(lds_offset(dst + f0 * 16)));
+        const int nr = min(n, last);
+        if (DSA_CHECK(row0 + nr >= 0, err_flag))
+          lds_dma16_s(uniform_ptr(gbase), uint32_t(nr * C::kKeyBytes + c * 16), lds_offset(dst + f0 * 16));
       }
     };
 
@@ -223,11 +273,11 @@ __global__ __launch_bounds__(kThreads, FP8 ? 4 : 1) void indexer_mfma(
     auto issue_kscale = [&](int t, int buf) {
       if constexpr (FP8) {
         constexpr int kPerWave = kKeyTile / kWaves;  // scales each wave stages
+        const int row0 = glo + t * kKeyTile;
         if (lane < kPerWave) {
-          const int key = glo + t * kKeyTile + kPerWave * wave + lane;
-          if (DSA_CHECK(key >= 0, err_flag))
-            lds_dma4_v(k_scale + (key < nk ? key : nk - 1),
-                       __builtin_amdgcn_readfirstlane(lds_offset(ks_tile[buf] + kPerWave * wave)));
+          const int nr = min(kPerWave * wave + lane, nk - 1 - row0);
+          if (DSA_CHECK(row0 + nr >= 0, err_flag))
+            lds_dma4_s(k_scale + row0, uint32_t(4 * nr), lds_offset(ks_tile[buf] + kPerWave * wave));
         }
       }
     };
@@ -243,21 +293,50 @@ __global__ __launch_bounds__(kThreads, FP8 ? 4 : 1) void indexer_mfma(
         issue_tile(t + 1, buf ^ 1);
       }
       const int key0 = glo + t * kKeyTile;
+      // fp8: lane-derived LDS addresses come from an opaque copy of the lane id, recomputed every
+      // tile rather than kept live across the loop. Kept live they are spilled, and a spill reload
+      // after this tile's direct loads were issued would wait for those loads as well (the wait
+      // counts loads in issue order).
+      int tl = lane;
+      if constexpr (FP8) asm volatile("" : "+v"(tl));
+      const int t32 = tl & 31, thalf = tl >> 5;
+      if constexpr (FP8) {
+        // c . k of block `wave` of this tile for the group's 8 queries (lane half h: queries
+        // 2j + h in output rows 8j + 4h + p), times k_scale, published for every wave
+        const unsigned char* tb = tiles + buf * C::kTileBytes;
+        const int n = 32 * wave + t32;
+        f32x16 L = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+          L = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(lin_a_operand(lin_rows, t32, ks, thalf),
+                                                              key_operand_lds<true>(tb, n, ks, thalf), L, 0, 0, 0, 127,
+                                                              0, 127);
+        const float ksn = ks_tile[buf][n];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int q = 2 * j + thalf;
+          lin_v[q * kLinPitch + n] = lin_combine(L, 4 * j, s_e0[q], ksn);
+        }
+        DSA_TILE_BARRIER_LDS();
+      }
       if (ok && key0 < hi_c && key0 + kKeyTile > lo_c) {  // wave-uniform
         const unsigned char* tb = tiles + buf * C::kTileBytes;
         // 32-key blocks; bf16 issues block nb+1's MFMAs before block nb's ReLU * w head-sum
         // epilogue, so the VALU epilogue runs under the matrix-core work
         auto block_mfma = [&](int nb, f32x16& a0, f32x16& a1) {
-          const int n = 32 * nb + l32;
-          block_mfma_chains<FP8>(qa, [&](int ks) { return key_operand_lds<FP8>(tb, n, ks); }, a0, a1);
+          const int n = 32 * nb + t32;
+          block_mfma_chains<FP8>(qa, [&](int ks) { return key_operand_lds<FP8>(tb, n, ks, thalf); }, a0, a1);
         };
         // lane holds key 32nb + l32 and heads 32m + 8(r/4) + 4half + r%4
         auto block_epilogue = [&](int nb, const f32x16& a0, const f32x16& a1) {
-          float sacc = block_head_sum(wv, a0, a1);
-          const int key = key0 + 32 * nb + l32;
-          const bool in = half == 0 && key >= lo_c && key < hi_c;
+          float sacc;
+          if constexpr (FP8)
+            sacc = fmaf(block_abs_sum(wv, a0, a1), ks_tile[buf][32 * nb + t32], lin_v[wave * kLinPitch + 32 * nb + t32]);
+          else
+            sacc = block_head_sum(wv, a0, a1);
+          const int key = key0 + 32 * nb + t32;
+          const bool in = thalf == 0 && key >= lo_c && key < hi_c;
           if (CAND && cand_row) {
-            if constexpr (FP8) sacc *= ks_tile[buf][32 * nb + l32];
             sacc += 0.f;  // -0.0 -> +0.0
             const bool hit = in && sacc >= theta_f;
             const uint64_t m = ballot(hit);
@@ -268,7 +347,6 @@ __global__ __launch_bounds__(kThreads, FP8 ? 4 : 1) void indexer_mfma(
               st_n += __popcll(m);
             }
           } else if (in && DSA_CHECK(key >= q_origin && key - q_origin < ld, err_flag)) {
-            if constexpr (FP8) sacc *= ks_tile[buf][32 * nb + l32];
             scores[int64_t(i) * ld + (key - q_origin)] = sacc + 0.f;  // -0.0 -> +0.0
           }
         };

@@ -1429,6 +1429,8 @@ __global__ __launch_bounds__(kStreamNT, 1) void topk_refill_kernel(
     int nk, int max_vis, int K, int window, int kv_row_base, int fuse_above, const int32_t* __restrict__ status,
     float* __restrict__ scratch, int64_t sld, int32_t* __restrict__ out) {
   __shared__ StreamShared sh;
+  // fp8: each wave's copy of the row's split c (kLinParts rows of 128 bytes)
+  __shared__ __attribute__((aligned(16))) unsigned char lin_rows[FP8 ? kStreamNT / 64 : 1][FP8 ? kLinParts * kIdxDim : 16];
   const int lane = threadIdx.x & 63, l32 = lane & 31, half = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   float* srow = scratch + int64_t(blockIdx.x) * sld;
@@ -1442,10 +1444,24 @@ __global__ __launch_bounds__(kStreamNT, 1) void topk_refill_kernel(
     typename IdxOps<FP8>::AOp qa[2][IdxOps<FP8>::kKsteps];
     float wv[2][16];
     load_query_operands<FP8>(qi, w, q_scale, row, qa, wv);
+    int e0 = 0;
+    if constexpr (FP8) {
+      // the indexer's fp8 arithmetic: halved weights and the row's split c (every wave its own copy)
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) wv[m][r] *= 0.5f;
+      uint32_t part[kLinParts];
+      e0 = lin_split(qi, wv, row, part);
+      if (half == 0) {
+#pragma unroll
+        for (int p = 0; p < kLinParts; ++p) lin_row_store(lin_rows[wave], p, l32, part[p]);
+      }
+    }
 #pragma unroll 1
     for (int b = wave; 32 * b < ev; b += kStreamNT / 64) {
       const int p = 32 * b + l32;
-      const float sc = key_score_global<FP8>(qa, wv, ki, k_scale, v.kv0 + min(p, ev - 1));
+      const float sc = key_score_global<FP8>(qa, wv, lin_rows[FP8 ? wave : 0], e0, ki, k_scale, v.kv0 + min(p, ev - 1));
       if (half == 0 && p < ev) srow[p] = sc;
     }
     __syncthreads();  // the row's scores are visible to the workgroup
