@@ -81,6 +81,9 @@ def test_candidate_lists_match_score_rows(name, kw, variant):
     ("inseq_cp8_last_8k", {"lens": (100000,), "topk": 16000}, False),   # lists overflow: every row recomputed
     ("inseq_cp8_last_8k", {"lens": (100000,)}, True),                    # every score 0.0: ties at the cut
     ("inseq_cp8_last_8k", {"lens": (100000,), "cp": 4, "rank": 3, "topk": 40000}, False),  # K above 32768
+    # fp8: the recomputation repeats the indexer's fp8 arithmetic (|x| head sum + split c . k)
+    ("long_131k_fp8", {"lens": (100000,), "topk": 16000}, False),
+    ("long_131k_fp8", {"lens": (100000,)}, True),
 ])
 def test_recomputed_rows_match_score_rows(name, kw, zero):
     dev = gpu()
