@@ -87,16 +87,20 @@ __device__ inline void block_mfma_chains(const typename IdxOps<FP8>::AOp (&qa)[2
   }
 }
 
-// sum over the 64 heads of w * relu(q . k) for the lane's key (both halves hold the result);
-// fp8 scores still need the key's scale
-__device__ inline float block_head_sum(const float (&wv)[2][16], const f32x16& a0, const f32x16& a1) {
+// this lane's half of the sum over the 64 heads of w * relu(q . k) (the 32 heads it holds)
+__device__ inline float block_head_part(const float (&wv)[2][16], const f32x16& a0, const f32x16& a1) {
   float sacc = 0.f;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     sacc = fmaf(wv[0][r], relu_bits(a0[r]), sacc);
     sacc = fmaf(wv[1][r], relu_bits(a1[r]), sacc);
   }
-  return xor32_sum(sacc);
+  return sacc;
+}
+// sum over the 64 heads of w * relu(q . k) for the lane's key (both halves hold the result);
+// fp8 scores still need the key's scale
+__device__ inline float block_head_sum(const float (&wv)[2][16], const f32x16& a0, const f32x16& a1) {
+  return xor32_sum(block_head_part(wv, a0, a1));
 }
 
 // ---- fp8: the score through ReLU(x) = (x + |x|) / 2 ----
@@ -185,15 +189,26 @@ __device__ inline float lin_combine(const f32x16& L, int b, int e0, float k_scal
   return r;
 }
 
-// sum over the 64 heads of w'' * |q . k| for the lane's key (both halves hold the result)
-__device__ inline float block_abs_sum(const float (&wv)[2][16], const f32x16& a0, const f32x16& a1) {
+// this lane's half of the sum over the 64 heads of w'' * |q . k| (the 32 heads it holds)
+__device__ inline float block_abs_part(const float (&wv)[2][16], const f32x16& a0, const f32x16& a1) {
   float sacc = 0.f;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     sacc = fmaf(wv[0][r], fabsf(a0[r]), sacc);
     sacc = fmaf(wv[1][r], fabsf(a1[r]), sacc);
   }
-  return xor32_sum(sacc);
+  return sacc;
+}
+// sum over the 64 heads of w'' * |q . k| for the lane's key (both halves hold the result)
+__device__ inline float block_abs_sum(const float (&wv)[2][16], const f32x16& a0, const f32x16& a1) {
+  return xor32_sum(block_abs_part(wv, a0, a1));
+}
+// Two blocks' head sums from their half sums pa and pb: lanes 0..31 get block a's (pa[l] +
+// pa[l + 32]), lanes 32..63 block b's (pb[l - 32] + pb[l]); one lane swap between the halves.
+// Each is the same float block_abs_sum gives (the same two halves added).
+__device__ inline float pair_sum(float pa, float pb) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(pa), __float_as_uint(pb), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // B operand of k-step ks read straight from key row `row` in global memory

@@ -235,6 +235,7 @@ __global__ __launch_bounds__(kThreads, FP8 ? 4 : 1) void indexer_mfma(
   const float theta_f = key_to_float(theta_k);
   const int seg_cap = cand_cap / int(gridDim.y);
   uint2* seg = CAND ? cand + int64_t(i) * cand_cap + int64_t(blockIdx.y) * seg_cap : nullptr;
+  float* srow = scores + int64_t(i) * ld;  // this query's score row (score-row mode)
   int st_n = 0;  // entries this wave found for its row (wave-uniform)
 #pragma unroll 1
   for (int64_t cs = int64_t(blockIdx.y) * chunk_keys; cs < int64_t(uhi) - ulo; cs += int64_t(gridDim.y) * chunk_keys) {
@@ -251,10 +252,10 @@ __global__ __launch_bounds__(kThreads, FP8 ? 4 : 1) void indexer_mfma(
       const int row0 = glo + t * kKeyTile;  // < nk: every range ends inside the key buffer
       const int last = nk - 1 - row0;
       const unsigned char* gbase = ki + int64_t(row0) * C::kKeyBytes;
-      // fp8 score rows: recomputed from an opaque copy of the lane id (the score-row epilogue
-      // leaves no registers to keep these offsets in; see the tile loop)
+      // recomputed from an opaque copy of the lane id where the kernel has no registers to keep
+      // these offsets in (all but the fp8 candidate kernel; see the tile loop)
       int ln = lane;
-      if constexpr (FP8 && !CAND) asm volatile("" : "+v"(ln));
+      if constexpr (!(FP8 && CAND)) asm volatile("" : "+v"(ln));
 #pragma unroll
       for (int j = 0; j < C::kLoads; ++j) {
         const int f0 = 64 * (C::kLoads * wave + j);
@@ -321,49 +322,56 @@ __global__ __launch_bounds__(kThreads, FP8 ? 4 : 1) void indexer_mfma(
       }
       if (ok && key0 < hi_c && key0 + kKeyTile > lo_c) {  // wave-uniform
         const unsigned char* tb = tiles + buf * C::kTileBytes;
-        // 32-key blocks; bf16 issues block nb+1's MFMAs before block nb's ReLU * w head-sum
-        // epilogue, so the VALU epilogue runs under the matrix-core work
+        // 32-key blocks; bf16 issues block nb+1's MFMAs before block nb's ReLU * w head sum, so
+        // the VALU work runs under the matrix-core work
         auto block_mfma = [&](int nb, f32x16& a0, f32x16& a1) {
           const int n = 32 * nb + t32;
           block_mfma_chains<FP8>(qa, [&](int ks) { return key_operand_lds<FP8>(tb, n, ks, thalf); }, a0, a1);
         };
-        // lane holds key 32nb + l32 and heads 32m + 8(r/4) + 4half + r%4
-        auto block_epilogue = [&](int nb, const f32x16& a0, const f32x16& a1) {
-          float sacc;
-          if constexpr (FP8)
-            sacc = fmaf(block_abs_sum(wv, a0, a1), ks_tile[buf][32 * nb + t32], lin_v[wave * kLinPitch + 32 * nb + t32]);
-          else
-            sacc = block_head_sum(wv, a0, a1);
-          const int key = key0 + 32 * nb + t32;
-          const bool in = thalf == 0 && key >= lo_c && key < hi_c;
+        // The MFMAs leave lane l with key 32nb + (l & 31) and heads 32m + 8(r/4) + 4(l/32) + r%4;
+        // the scores are emitted two blocks at a time: pair_sum puts block nb's score in half 0
+        // and block nb + 1's in half 1, so every lane emits a key of its own.
+        auto emit = [&](int nb, float hsum) {
+          const int n = 32 * (nb + thalf) + t32;
+          float sacc = hsum;
+          if constexpr (FP8) sacc = fmaf(hsum, ks_tile[buf][n], lin_v[wave * kLinPitch + n]);
+          const int key = key0 + n;
+          const bool in = key >= lo_c && key < hi_c;
           if (CAND && cand_row) {
             sacc += 0.f;  // -0.0 -> +0.0
             const bool hit = in && sacc >= theta_f;
             const uint64_t m = ballot(hit);
             if (m) {
               const int slot = st_n + lanes_below(m);
-              if (hit && slot < seg_cap && DSA_CHECK(key >= q_origin, err_flag))
-                seg[slot] = make_uint2(__float_as_uint(sacc), uint32_t(key - q_origin));
+              if (hit && slot < seg_cap && DSA_CHECK(key >= q_origin, err_flag))  // 32-bit offset, scalar base
+                *reinterpret_cast<uint2*>(reinterpret_cast<unsigned char*>(seg) + uint32_t(slot) * 8u) =
+                    make_uint2(__float_as_uint(sacc), uint32_t(key - q_origin));
               st_n += __popcll(m);
             }
           } else if (in && DSA_CHECK(key >= q_origin && key - q_origin < ld, err_flag)) {
-            scores[int64_t(i) * ld + (key - q_origin)] = sacc + 0.f;  // -0.0 -> +0.0
+            srow[uint32_t(key - q_origin)] = sacc + 0.f;  // -0.0 -> +0.0
           }
         };
         if constexpr (!FP8) {
           f32x16 acc[2][2];
+          float part = 0.f;  // the previous block's half sum
           block_mfma(0, acc[0][0], acc[0][1]);
 #pragma unroll
           for (int nb = 0; nb < kKeyTile / 32; ++nb) {
             if (nb + 1 < kKeyTile / 32) block_mfma(nb + 1, acc[(nb + 1) & 1][0], acc[(nb + 1) & 1][1]);
-            block_epilogue(nb, acc[nb & 1][0], acc[nb & 1][1]);
+            const float p = block_head_part(wv, acc[nb & 1][0], acc[nb & 1][1]);
+            if (nb & 1) emit(nb - 1, pair_sum(part, p));
+            else part = p;
           }
         } else {
+          float part = 0.f;  // the previous block's half sum
 #pragma unroll
           for (int nb = 0; nb < kKeyTile / 32; ++nb) {
             f32x16 acc0, acc1;
             block_mfma(nb, acc0, acc1);
-            block_epilogue(nb, acc0, acc1);
+            const float p = block_abs_part(wv, acc0, acc1);
+            if (nb & 1) emit(nb - 1, pair_sum(part, p));
+            else part = p;
           }
         }
       }
