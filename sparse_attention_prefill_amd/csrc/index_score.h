@@ -275,7 +275,10 @@ __device__ inline float key_score_global(const typename IdxOps<FP8>::AOp (&qa)[2
     // the linear part first (its accumulators are dead before the head chains start); output
     // rows 8j + 4h + p all read part p, so L[p] is P_p . k in both halves
     f32x16 L = f32x16{};
-    const int l32 = threadIdx.x & 31;
+    // read here for every key block (an opaque lane index keeps the compiler from holding this
+    // 16-register operand across the caller's loop)
+    int l32 = threadIdx.x & 31;
+    asm volatile("" : "+v"(l32));
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
       L = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(lin_a_operand(lin_rows, l32 & (kLinParts - 1), ks),
