@@ -174,6 +174,57 @@ def test_indexer_scores(name, kw, variant):
     _indexer_case(S.WORKLOADS[name].with_(**kw), variant, dev)
 
 
+# Scaling every weight by 2^k scales every score by exactly 2^k (each step of the score's
+# arithmetic commutes with a power-of-two scale while nothing over- or underflows: the halved
+# weights, the head sums, fp8's split c = sum_h (w_h/2) q_h and its scale exponent, the final FMA),
+# so the GPU scores must match bit for bit and the candidate-list ids must not move. The scales
+# reach magnitudes the Gaussian cases never do, where a wrong exponent or clamp in the split of c
+# would show.
+@pytest.mark.parametrize("name,kw", [
+    ("long_131k_fp8", {"lens": (3000,)}),
+    ("long_131k_fp8", {"lens": (100000,)}),          # candidate lists (rows > 98 304 keys)
+    ("inseq_cp8_last_8k", {"lens": (3000,)}),        # bf16
+])
+def test_indexer_scores_scale_exactly_with_the_weights(name, kw):
+    import sparse_attention_prefill_amd as D
+    dev = gpu()
+    wl = S.WORKLOADS[name].with_(**kw)
+    m = O.cp_metadata(wl.qsl, wl.seq_lens, wl.cp, wl.rank, wl.mode, wl.pad)
+    toks = m["token_map"][m["token_map"] >= 0]
+    inp = S.stream_inputs(wl, "normal")
+    qin = S.query_inputs(wl, toks, "normal", indexer_only=True)
+    kind = wl.idx_dtype
+    max_kv = int(m["local_seq_lens"].max())
+    ld = (max_kv + 63) // 64 * 64
+    base = [to_dev(qin["q_idx"], kind, dev), None, to_dev(inp["k_idx"], kind, dev),
+            to_dev(m["local_query_start_loc"], "i32", dev), to_dev(m["local_seq_lens"], "i32", dev),
+            to_dev(m["local_kv_start_loc"], "i32", dev), max_kv]
+    kw_ = dict(q_stride=m["stride"],
+               q_scale=to_dev(qin["q_scale"], "f32", dev) if "q_scale" in qin else None,
+               k_scale=to_dev(inp["k_scale"], "f32", dev) if "k_scale" in inp else None)
+    w = qin["w"].astype(np.float32)
+    nq = len(toks)
+    rows = np.arange(nq) if nq <= 512 else np.unique(np.concatenate([np.arange(32), np.arange(nq - 32, nq),
+                                                                      np.linspace(0, nq - 1, 64).astype(int)]))
+    sel = torch.from_numpy(rows).to(dev)
+    res = {}
+    for k in (0, -40, 40):
+        args = list(base)
+        args[1] = to_dev(np.ldexp(w, k).astype(np.float32), "f32", dev)
+        scores = torch.empty(nq, ld, dtype=torch.float32, device=dev)
+        D.indexer_scores(*args, scores, **kw_)
+        ids = D.indexer_topk(*args, topk=wl.topk, **kw_)
+        torch.cuda.synchronize()
+        res[k] = (scores[sel].cpu().numpy(), ids.cpu().numpy())
+        del scores
+    views = O.query_views(m)
+    for k in (-40, 40):
+        for n, i in enumerate(rows):
+            E = views[i][1]
+            assert np.array_equal(res[k][0][n, :E], np.ldexp(res[0][0][n, :E], k)), (name, k, int(i))
+        assert np.array_equal(res[k][1], res[0][1]), (name, k)
+
+
 # Head dimensions that take the generic indexer's other paths: not a multiple of 4 or over 64
 # (key rows re-read per head), 48 (held in registers, a 64-slot row with the tail unused), and
 # bf16 rows of 64 read 4 elements at a time.
