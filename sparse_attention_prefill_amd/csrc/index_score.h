@@ -1,5 +1,7 @@
-// Lightning-indexer score arithmetic on gfx950 matrix cores, shared by every kernel that computes
-// a score, so that a (query, key) score is the same float whichever kernel produced it.
+// Lightning-indexer score arithmetic on gfx950 matrix cores, shared by every kernel that emits a
+// score (the indexer and the recomputation of unusable candidate rows), so that a (query, key)
+// score is the same float whichever of them produced it. The threshold sample of fp8 candidate rows
+// keeps the ReLU form below: it only places a threshold.
 //
 // [xLLM-CP] "feat: DeepSeek-V4 DSA context-parallel on NPU", Design, data-flow step (3):
 //   score(i, s) = sum_h w[i,h] * max(0, q_idx[i,h,:] . k_idx[s,:])   (64 heads x 128)
@@ -114,9 +116,9 @@ __device__ inline float block_head_sum(const float (&wv)[2][16], const f32x16& a
 // Every split step is exact: P_pd is the running remainder (in units of 2^e0 16^-p, below 256 in
 // magnitude) rounded to E4M3 (round to nearest even, so within 8 units), remainder - P_pd is exact
 // in fp32 (Sterbenz: the two are within a factor of two, or P_pd is 0), and the scaling by 16 that
-// gives the next remainder (below 128) is exact. fp8 scores of every kernel go through lin_split /
-// lin_combine / block_abs_sum in this order, so a (query, key) score is the same float whichever
-// kernel computed it.
+// gives the next remainder (below 128) is exact. The indexer and the recomputation both go through
+// lin_split, lin_combine and the |x| half sums (block_abs_part, the two halves then added), so an fp8
+// score is the same float whichever of them computed it.
 constexpr int kLinParts = 4;
 
 // The four dimensions 4 (lane & 31) .. +3 of c for query i, in both halves of the wave, split into
