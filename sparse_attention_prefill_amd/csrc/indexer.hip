@@ -237,147 +237,191 @@ __global__ __launch_bounds__(kThreads, FP8 ? 4 : 1) void indexer_mfma(
   uint2* seg = CAND ? cand + int64_t(i) * cand_cap + int64_t(blockIdx.y) * seg_cap : nullptr;
   float* srow = scores + int64_t(i) * ld;  // this query's score row (score-row mode)
   int st_n = 0;  // entries this wave found for its row (wave-uniform)
+  // The key sweep, compiled once per epilogue (candidate list or score row) so that the per-key
+  // code holds no test of the wave-uniform choice between them.
+  auto sweep = [&](auto list_tag) {
+    constexpr bool LIST = decltype(list_tag)::value;
 #pragma unroll 1
-  for (int64_t cs = int64_t(blockIdx.y) * chunk_keys; cs < int64_t(uhi) - ulo; cs += int64_t(gridDim.y) * chunk_keys) {
-    const int glo = ulo + int(cs);
-    const int ghi = int(min(int64_t(uhi), int64_t(glo) + chunk_keys));
-    const int lo_c = max(lo, glo), hi_c = min(hi, ghi);
-    const int n_tiles = (ghi - glo + kKeyTile - 1) / kKeyTile;
-    // ---- staging: tile t holds keys glo + 256t + [0, 256); lane loads 16-byte chunks ----
-    // Addresses are a wave-uniform base (scalar registers) plus a 32-bit lane offset, which keeps
-    // the per-lane part to one register per load. Rows past the key buffer read its last row (the
-    // tile may run past the chunk's end).
-    auto issue_tile = [&](int t, int buf) {
-      unsigned char* dst = tiles + buf * C::kTileBytes;
-      const int row0 = glo + t * kKeyTile;  // < nk: every range ends inside the key buffer
-      const int last = nk - 1 - row0;
-      const unsigned char* gbase = ki + int64_t(row0) * C::kKeyBytes;
-      // recomputed from an opaque copy of the lane id where the kernel has no registers to keep
-      // these offsets in (all but the fp8 candidate kernel; see the tile loop)
-      int ln = lane;
-      if constexpr (!(FP8 && CAND)) asm volatile("" : "+v"(ln));
+    for (int64_t cs = int64_t(blockIdx.y) * chunk_keys; cs < int64_t(uhi) - ulo;
+         cs += int64_t(gridDim.y) * chunk_keys) {
+      const int glo = ulo + int(cs);
+      const int ghi = int(min(int64_t(uhi), int64_t(glo) + chunk_keys));
+      const int lo_c = max(lo, glo), hi_c = min(hi, ghi);
+      const uint32_t n_in = uint32_t(max(hi_c - lo_c, 0));  // key - lo_c < n_in (unsigned): key in [lo_c, hi_c)
+      const int n_tiles = (ghi - glo + kKeyTile - 1) / kKeyTile;
+      // ---- staging: tile t holds keys glo + 256t + [0, 256); lane loads 16-byte chunks ----
+      // Addresses are a wave-uniform base (scalar registers) plus a 32-bit lane offset, which keeps
+      // the per-lane part to one register per load. Rows past the key buffer read its last row (the
+      // tile may run past the chunk's end).
+      auto issue_tile = [&](int t, int buf) {
+        unsigned char* dst = tiles + buf * C::kTileBytes;
+        const int row0 = glo + t * kKeyTile;  // < nk: every range ends inside the key buffer
+        const int last = nk - 1 - row0;
+        const unsigned char* gbase = ki + int64_t(row0) * C::kKeyBytes;
+        if constexpr (FP8) {
+          if (last >= kKeyTile - 1) {  // wave-uniform: every row of the tile is inside the key buffer
+            // load j of this wave covers row n0 + 8j, chunk lane % 8, with n0 = 32 wave + lane / 8;
+            // the swizzle reads row bits 0..3, so only bit 3 (j odd) changes it
+            const int n0 = 32 * wave + (lane >> 3);
+            const uint32_t b0 = uint32_t(n0 * C::kKeyBytes + kswz<C::kChunks>(n0, lane & 7) * 16);
+            const uint32_t b1 = uint32_t(n0 * C::kKeyBytes + kswz<C::kChunks>(n0 + 8, lane & 7) * 16);
 #pragma unroll
-      for (int j = 0; j < C::kLoads; ++j) {
-        const int f0 = 64 * (C::kLoads * wave + j);
-        const int f = f0 + ln;
-        const int n = f / C::kChunks;
-        const int cp = f - n * C::kChunks;
-        const int c = kswz<C::kChunks>(n, cp);
-        const int nr = min(n, last);
-        if (DSA_CHECK(row0 + nr >= 0, err_flag))
-          lds_dma16_s(uniform_ptr(gbase), uint32_t(nr * C::kKeyBytes + c * 16), lds_offset(dst + f0 * 16));
-      }
-    };
-
-    // fp8: the tile's per-key scales are staged next to it in LDS: wave w copies keys
-    // [32w, 32w + 32) with one more direct load (32 active lanes of 4 bytes)
-    auto issue_kscale = [&](int t, int buf) {
-      if constexpr (FP8) {
-        constexpr int kPerWave = kKeyTile / kWaves;  // scales each wave stages
-        const int row0 = glo + t * kKeyTile;
-        if (lane < kPerWave) {
-          const int nr = min(kPerWave * wave + lane, nk - 1 - row0);
+            for (int j = 0; j < C::kLoads; ++j)
+              lds_dma16_s(uniform_ptr(gbase), ((j & 1) ? b1 : b0) + 8u * C::kKeyBytes * j,
+                          lds_offset(dst + 64 * (C::kLoads * wave + j) * 16));
+            return;
+          }
+        }
+        // recomputed from an opaque copy of the lane id: the kernels have no registers to keep
+        // these offsets in across the tile loop
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+#pragma unroll
+        for (int j = 0; j < C::kLoads; ++j) {
+          const int f0 = 64 * (C::kLoads * wave + j);
+          const int f = f0 + ln;
+          const int n = f / C::kChunks;
+          const int cp = f - n * C::kChunks;
+          const int c = kswz<C::kChunks>(n, cp);
+          const int nr = min(n, last);
           if (DSA_CHECK(row0 + nr >= 0, err_flag))
-            lds_dma4_s(k_scale + row0, uint32_t(4 * nr), lds_offset(ks_tile[buf] + kPerWave * wave));
+            lds_dma16_s(uniform_ptr(gbase), uint32_t(nr * C::kKeyBytes + c * 16), lds_offset(dst + f0 * 16));
         }
-      }
-    };
-    issue_kscale(0, 0);
-    issue_tile(0, 0);
-    for (int t = 0; t < n_tiles; ++t) {
-      const int buf = t & 1;
-      // One barrier per tile: after it, tile t has landed for every wave and every wave is done
-      // with tile t - 1, whose buffer then takes tile t + 1 (loaded while tile t is computed).
-      DSA_TILE_BARRIER_ALL();
-      if (t + 1 < n_tiles) {
-        issue_kscale(t + 1, buf ^ 1);
-        issue_tile(t + 1, buf ^ 1);
-      }
-      const int key0 = glo + t * kKeyTile;
-      // fp8: lane-derived LDS addresses come from an opaque copy of the lane id, recomputed every
-      // tile rather than kept live across the loop. Kept live they are spilled, and a spill reload
-      // after this tile's direct loads were issued would wait for those loads as well (the wait
-      // counts loads in issue order).
-      int tl = lane;
-      if constexpr (FP8) asm volatile("" : "+v"(tl));
-      const int t32 = tl & 31, thalf = tl >> 5;
-      if constexpr (FP8) {
-        // c . k of block `wave` of this tile for the group's 8 queries (lane half h: queries
-        // 2j + h in output rows 8j + 4h + p), times k_scale, published for every wave
-        const unsigned char* tb = tiles + buf * C::kTileBytes;
-        const int n = 32 * wave + t32;
-        f32x16 L = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-          L = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(lin_a_operand(lin_rows, t32, ks, thalf),
-                                                              key_operand_lds<true>(tb, n, ks, thalf), L, 0, 0, 0, 127,
-                                                              0, 127);
-        const float ksn = ks_tile[buf][n];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int q = 2 * j + thalf;
-          lin_v[q * kLinPitch + n] = lin_combine(L, 4 * j, s_e0[q], ksn);
+      };
+
+      // fp8: the tile's per-key scales are staged next to it in LDS: wave w copies keys
+      // [32w, 32w + 32) with one more direct load (32 active lanes of 4 bytes)
+      auto issue_kscale = [&](int t, int buf) {
+        if constexpr (FP8) {
+          constexpr int kPerWave = kKeyTile / kWaves;  // scales each wave stages
+          const int row0 = glo + t * kKeyTile;
+          if (lane < kPerWave) {
+            const int nr = min(kPerWave * wave + lane, nk - 1 - row0);
+            if (DSA_CHECK(row0 + nr >= 0, err_flag))
+              lds_dma4_s(k_scale + row0, uint32_t(4 * nr), lds_offset(ks_tile[buf] + kPerWave * wave));
+          }
         }
-        DSA_TILE_BARRIER_LDS();
-      }
-      if (ok && key0 < hi_c && key0 + kKeyTile > lo_c) {  // wave-uniform
-        const unsigned char* tb = tiles + buf * C::kTileBytes;
-        // 32-key blocks; bf16 issues block nb+1's MFMAs before block nb's ReLU * w head sum, so
-        // the VALU work runs under the matrix-core work
-        auto block_mfma = [&](int nb, f32x16& a0, f32x16& a1) {
-          const int n = 32 * nb + t32;
-          block_mfma_chains<FP8>(qa, [&](int ks) { return key_operand_lds<FP8>(tb, n, ks, thalf); }, a0, a1);
+      };
+      issue_kscale(0, 0);
+      issue_tile(0, 0);
+      for (int t = 0; t < n_tiles; ++t) {
+        const int buf = t & 1;
+        // One barrier per tile: after it, tile t has landed for every wave and every wave is done
+        // with tile t - 1, whose buffer then takes tile t + 1 (loaded while tile t is computed).
+        DSA_TILE_BARRIER_ALL();
+        if (t + 1 < n_tiles) {
+          issue_kscale(t + 1, buf ^ 1);
+          issue_tile(t + 1, buf ^ 1);
+        }
+        const int key0 = glo + t * kKeyTile;
+        // fp8: lane-derived LDS addresses come from an opaque copy of the lane id, recomputed every
+        // tile rather than kept live across the loop. Kept live they are spilled, and a spill reload
+        // after this tile's direct loads were issued would wait for those loads as well (the wait
+        // counts loads in issue order).
+        int tl = lane;
+        if constexpr (FP8) asm volatile("" : "+v"(tl));
+        const int t32 = tl & 31, thalf = tl >> 5;
+        // fp8: this lane's B-operand chunk addresses for key row t32 of the tile ([k-step][chunk]);
+        // row 32 nb + t32 is 4096 nb bytes further (the swizzle reads row bits 0..3 only)
+        const unsigned char* kp[2][2];
+        if constexpr (FP8) {
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+              kp[ks][x] = tiles + buf * C::kTileBytes + t32 * C::kKeyBytes +
+                          kswz<C::kChunks>(t32, 4 * ks + 2 * thalf + x) * 16;
+        }
+        auto fp8_key_op = [&](int nb, int ks) {
+          const i32x4 x0 = *reinterpret_cast<const i32x4*>(kp[ks][0] + 32 * C::kKeyBytes * nb);
+          const i32x4 x1 = *reinterpret_cast<const i32x4*>(kp[ks][1] + 32 * C::kKeyBytes * nb);
+          return i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
         };
-        // The MFMAs leave lane l with key 32nb + (l & 31) and heads 32m + 8(r/4) + 4(l/32) + r%4;
-        // the scores are emitted two blocks at a time: pair_sum puts block nb's score in half 0
-        // and block nb + 1's in half 1, so every lane emits a key of its own.
-        auto emit = [&](int nb, float hsum) {
-          const int n = 32 * (nb + thalf) + t32;
-          float sacc = hsum;
-          if constexpr (FP8) sacc = fmaf(hsum, ks_tile[buf][n], lin_v[wave * kLinPitch + n]);
-          const int key = key0 + n;
-          const bool in = key >= lo_c && key < hi_c;
-          if (CAND && cand_row) {
-            sacc += 0.f;  // -0.0 -> +0.0
-            const bool hit = in && sacc >= theta_f;
-            const uint64_t m = ballot(hit);
-            if (m) {
-              const int slot = st_n + lanes_below(m);
-              if (hit && slot < seg_cap && DSA_CHECK(key >= q_origin, err_flag))  // 32-bit offset, scalar base
-                *reinterpret_cast<uint2*>(reinterpret_cast<unsigned char*>(seg) + uint32_t(slot) * 8u) =
-                    make_uint2(__float_as_uint(sacc), uint32_t(key - q_origin));
-              st_n += __popcll(m);
+        if constexpr (FP8) {
+          // c . k of block `wave` of this tile for the group's 8 queries (lane half h: queries
+          // 2j + h in output rows 8j + 4h + p), times k_scale, published for every wave
+          const int n = 32 * wave + t32;
+          f32x16 L = f32x16{};
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+            L = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(lin_a_operand(lin_rows, t32, ks, thalf),
+                                                                fp8_key_op(wave, ks), L, 0, 0, 0, 127, 0, 127);
+          const float ksn = ks_tile[buf][n];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int q = 2 * j + thalf;
+            lin_v[q * kLinPitch + n] = lin_combine(L, 4 * j, s_e0[q], ksn);
+          }
+          DSA_TILE_BARRIER_LDS();
+        }
+        if (ok && key0 < hi_c && key0 + kKeyTile > lo_c) {  // wave-uniform
+          const unsigned char* tb = tiles + buf * C::kTileBytes;
+          // 32-key blocks; bf16 issues block nb+1's MFMAs before block nb's ReLU * w head sum, so
+          // the VALU work runs under the matrix-core work
+          auto block_mfma = [&](int nb, f32x16& a0, f32x16& a1) {
+            const int n = 32 * nb + t32;
+            if constexpr (FP8) block_mfma_chains<FP8>(qa, [&](int ks) { return fp8_key_op(nb, ks); }, a0, a1);
+            else block_mfma_chains<FP8>(qa, [&](int ks) { return key_operand_lds<FP8>(tb, n, ks, thalf); }, a0, a1);
+          };
+          // fp8: this lane's key scale and linear part for key tl of the tile (block pair nb, nb + 1
+          // at 32 nb floats further)
+          const float* ksp = ks_tile[buf] + tl;
+          const float* lvp = lin_v + wave * kLinPitch + tl;
+          // The MFMAs leave lane l with key 32nb + (l & 31) and heads 32m + 8(r/4) + 4(l/32) + r%4;
+          // the scores are emitted two blocks at a time: pair_sum puts block nb's score in half 0
+          // and block nb + 1's in half 1, so every lane emits a key of its own.
+          auto emit = [&](int nb, float hsum) {
+            // lane tl holds key 32 nb + tl of the tile (n = 32 (nb + thalf) + t32)
+            float sacc = hsum;
+            if constexpr (FP8) sacc = fmaf(hsum, ksp[32 * nb], lvp[32 * nb]);
+            const int key = key0 + 32 * nb + tl;
+            const bool in = uint32_t(key0 + 32 * nb - lo_c) + uint32_t(tl) < n_in;
+            if constexpr (LIST) {
+              sacc += 0.f;  // -0.0 -> +0.0
+              const bool hit = in && sacc >= theta_f;
+              // two compares straight into lane masks (the ballot of their conjunction would go
+              // through a 0/1 register and a third compare)
+              const uint64_t m = ballot(in) & ballot(sacc >= theta_f);
+              if (m) {
+                const int slot = st_n + lanes_below(m);
+                if (hit && slot < seg_cap && DSA_CHECK(key >= q_origin, err_flag))  // 32-bit offset, scalar base
+                  *reinterpret_cast<uint2*>(reinterpret_cast<unsigned char*>(seg) + uint32_t(slot) * 8u) =
+                      make_uint2(__float_as_uint(sacc), uint32_t(key0 + 32 * nb - q_origin) + uint32_t(tl));
+                st_n += __popcll(m);
+              }
+            } else if (in && DSA_CHECK(key >= q_origin && key - q_origin < ld, err_flag)) {
+              srow[uint32_t(key - q_origin)] = sacc + 0.f;  // -0.0 -> +0.0
             }
-          } else if (in && DSA_CHECK(key >= q_origin && key - q_origin < ld, err_flag)) {
-            srow[uint32_t(key - q_origin)] = sacc + 0.f;  // -0.0 -> +0.0
-          }
-        };
-        if constexpr (!FP8) {
-          f32x16 acc[2][2];
-          float part = 0.f;  // the previous block's half sum
-          block_mfma(0, acc[0][0], acc[0][1]);
+          };
+          if constexpr (!FP8) {
+            f32x16 acc[2][2];
+            float part = 0.f;  // the previous block's half sum
+            block_mfma(0, acc[0][0], acc[0][1]);
 #pragma unroll
-          for (int nb = 0; nb < kKeyTile / 32; ++nb) {
-            if (nb + 1 < kKeyTile / 32) block_mfma(nb + 1, acc[(nb + 1) & 1][0], acc[(nb + 1) & 1][1]);
-            const float p = block_head_part(wv, acc[nb & 1][0], acc[nb & 1][1]);
-            if (nb & 1) emit(nb - 1, pair_sum(part, p));
-            else part = p;
-          }
-        } else {
-          float part = 0.f;  // the previous block's half sum
+            for (int nb = 0; nb < kKeyTile / 32; ++nb) {
+              if (nb + 1 < kKeyTile / 32) block_mfma(nb + 1, acc[(nb + 1) & 1][0], acc[(nb + 1) & 1][1]);
+              const float p = block_head_part(wv, acc[nb & 1][0], acc[nb & 1][1]);
+              if (nb & 1) emit(nb - 1, pair_sum(part, p));
+              else part = p;
+            }
+          } else {
+            float part = 0.f;  // the previous block's half sum
 #pragma unroll
-          for (int nb = 0; nb < kKeyTile / 32; ++nb) {
-            f32x16 acc0, acc1;
-            block_mfma(nb, acc0, acc1);
-            const float p = block_abs_part(wv, acc0, acc1);
-            if (nb & 1) emit(nb - 1, pair_sum(part, p));
-            else part = p;
+            for (int nb = 0; nb < kKeyTile / 32; ++nb) {
+              f32x16 acc0, acc1;
+              block_mfma(nb, acc0, acc1);
+              const float p = block_abs_part(wv, acc0, acc1);
+              if (nb & 1) emit(nb - 1, pair_sum(part, p));
+              else part = p;
+            }
           }
         }
       }
+      DSA_TILE_BARRIER_LDS();  // every wave is done with this chunk's buffers before the next chunk's first tile
     }
-    DSA_TILE_BARRIER_LDS();  // every wave is done with this chunk's buffers before the next chunk's first tile
-  }
+  };
+  if (cand_row) sweep(std::true_type{});
+  else sweep(std::false_type{});
   if (CAND && cand_row && lane == 0) n_cand[int64_t(i) * gridDim.y + blockIdx.y] = st_n;
 }
 
