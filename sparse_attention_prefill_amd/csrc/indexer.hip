@@ -265,10 +265,12 @@ __global__ __launch_bounds__(kThreads, FP8 ? 4 : 1) void indexer_mfma(
             const int n0 = 32 * wave + (lane >> 3);
             const uint32_t b0 = uint32_t(n0 * C::kKeyBytes + kswz<C::kChunks>(n0, lane & 7) * 16);
             const uint32_t b1 = uint32_t(n0 * C::kKeyBytes + kswz<C::kChunks>(n0 + 8, lane & 7) * 16);
+            if (DSA_CHECK(row0 >= 0, err_flag)) {
 #pragma unroll
-            for (int j = 0; j < C::kLoads; ++j)
-              lds_dma16_s(uniform_ptr(gbase), ((j & 1) ? b1 : b0) + 8u * C::kKeyBytes * j,
-                          lds_offset(dst + 64 * (C::kLoads * wave + j) * 16));
+              for (int j = 0; j < C::kLoads; ++j)
+                lds_dma16_s(uniform_ptr(gbase), ((j & 1) ? b1 : b0) + 8u * C::kKeyBytes * j,
+                            lds_offset(dst + 64 * (C::kLoads * wave + j) * 16));
+            }
             return;
           }
         }
