@@ -1,7 +1,8 @@
 // Lightning-indexer score arithmetic on gfx950 matrix cores, shared by every kernel that emits a
-// score (the indexer and the recomputation of unusable candidate rows), so that a (query, key)
-// score is the same float whichever of them produced it. The threshold sample of fp8 candidate rows
-// keeps the ReLU form below: it only places a threshold.
+// score (the indexer, the recomputation of unusable candidate rows and the threshold sample of
+// candidate rows), so that a (query, key) score is the same float whichever of them produced it.
+// The one exception: fp8 threshold samples of a group of rows that do not share their sample keys
+// keep the ReLU form below (they only place a threshold).
 //
 // [xLLM-CP] "feat: DeepSeek-V4 DSA context-parallel on NPU", Design, data-flow step (3):
 //   score(i, s) = sum_h w[i,h] * max(0, q_idx[i,h,:] . k_idx[s,:])   (64 heads x 128)
@@ -116,9 +117,9 @@ __device__ inline float block_head_sum(const float (&wv)[2][16], const f32x16& a
 // Every split step is exact: P_pd is the running remainder (in units of 2^e0 16^-p, below 256 in
 // magnitude) rounded to E4M3 (round to nearest even, so within 8 units), remainder - P_pd is exact
 // in fp32 (Sterbenz: the two are within a factor of two, or P_pd is 0), and the scaling by 16 that
-// gives the next remainder (below 128) is exact. The indexer and the recomputation both go through
-// lin_split, lin_combine and the |x| half sums (block_abs_part, the two halves then added), so an fp8
-// score is the same float whichever of them computed it.
+// gives the next remainder (below 128) is exact. The indexer, the recomputation and the shared
+// threshold sample all go through lin_split, lin_combine and the |x| half sums (block_abs_part, the
+// two halves then added), so an fp8 score is the same float whichever of them computed it.
 constexpr int kLinParts = 4;
 
 // The four dimensions 4 (lane & 31) .. +3 of c for query i, in both halves of the wave, split into
@@ -225,6 +226,21 @@ __device__ inline typename IdxOps<FP8>::AOp key_operand_global(const unsigned ch
   } else {
     return *reinterpret_cast<const bf16x8*>(p + 2 * (16 * ks + 8 * half));
   }
+}
+
+// A wave-uniform pointer, in scalar registers whatever the compiler could prove about it.
+__device__ inline const void* uniform_ptr(const void* p) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(u));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(u >> 32));
+  return reinterpret_cast<const void*>((uint64_t(hi) << 32) | lo);
+}
+// Direct global->LDS 4-byte loads from a uniform base and a per-lane byte offset: lane l's word
+// lands at lds_base + 4*l (M0 is written only here and in the other direct-load helpers).
+__device__ inline void lds_dma4_s(const void* gbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(uniform_ptr(gbase)),
+               "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory", "m0");
 }
 
 // Physical 16-byte chunk of logical chunk c of key row n in an LDS key tile. 256-byte rows

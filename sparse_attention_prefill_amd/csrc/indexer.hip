@@ -102,21 +102,6 @@ __global__ __launch_bounds__(kGenThreads) void indexer_generic(
   scores[int64_t(i) * ld + s] = acc + 0.f;  // -0.0 -> +0.0
 }
 
-// A wave-uniform pointer, in scalar registers whatever the compiler could prove about it.
-__device__ inline const void* uniform_ptr(const void* p) {
-  const uint64_t u = reinterpret_cast<uint64_t>(p);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(u));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(u >> 32));
-  return reinterpret_cast<const void*>((uint64_t(hi) << 32) | lo);
-}
-// Direct global->LDS 4-byte loads from a uniform base and a per-lane byte offset: lane l's word
-// lands at lds_base + 4*l (M0 is written only here and in the other direct-load helpers).
-__device__ inline void lds_dma4_s(const void* gbase, uint32_t voff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(uniform_ptr(gbase)),
-               "s"(__builtin_amdgcn_readfirstlane(lds_base))
-               : "memory", "m0");
-}
-
 // ---------------------------------------------------------------------------------------------
 // MFMA kernel: 64 heads x 128
 // ---------------------------------------------------------------------------------------------

@@ -1141,9 +1141,11 @@ constexpr int kCandEPT = kFuseCap / kCandNT;           // 16 list entries per th
 // are recomputed) while holding about K + 5.5 sqrt(K ev / m) ev / m entries. When the 8 rows of
 // the workgroup are candidate rows of one request they share the sample positions (those of the
 // shortest row) and each tile is staged once in LDS; otherwise each wave reads its own keys.
-// Also zeroes every row's list-segment counts.
+// Shared fp8 samples are scored with the indexer's arithmetic (|x| head sums, the linear part on
+// the matrix cores for the 8 rows at once), so they are the indexer's floats; the per-wave path
+// keeps the ReLU form. Also zeroes every row's list-segment counts.
 template <bool FP8>
-__global__ __launch_bounds__(512) void topk_theta_kernel(
+__global__ __launch_bounds__(512, FP8 ? 4 : 1) void topk_theta_kernel(
     const unsigned char* __restrict__ qi, const float* __restrict__ q_scale, const float* __restrict__ w,
     const unsigned char* __restrict__ ki, const float* __restrict__ k_scale, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ used_kv, const int32_t* __restrict__ cu_kv, int batch, int stride, int ratio, int nq,
@@ -1162,7 +1164,13 @@ __global__ __launch_bounds__(512) void topk_theta_kernel(
     alignas(16) unsigned char tiles[kBufs][kTileBytes];
   } u;
   __shared__ alignas(16) float ks_tiles[kBufs][FP8 ? 128 : 4];
-  __shared__ int s_kv0[8], s_ev[8];
+  // fp8 shared path: the group's split c rows (row 8j + 4h + p: part p of row 2j + h) and each
+  // tile's linear parts c . k times k_scale, [row][key of the tile] (pitch: the two lane halves
+  // write rows 2j and 2j + 1 at once, 32 banks apart)
+  constexpr int kLinPitch = 128 + 32;
+  __shared__ alignas(16) unsigned char lin_rows[FP8 ? 32 * kIdxDim : 16];
+  __shared__ alignas(16) float lin_v[FP8 ? 8 * kLinPitch : 4];
+  __shared__ int s_kv0[8], s_ev[8], s_e0[8];
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int i = blockIdx.x * 8 + wave;
@@ -1197,6 +1205,23 @@ __global__ __launch_bounds__(512) void topk_theta_kernel(
   typename IdxOps<FP8>::AOp qa[2][IdxOps<FP8>::kKsteps];
   float wv[2][16];
   load_query_operands<FP8>(qi, w, q_scale, i, qa, wv);
+  // fp8 shared path: the indexer's arithmetic (score = sum_h w'' |x_h| + c . k, w'' = w q_scale / 2,
+  // the linear part on the matrix cores for the group's 8 rows), so the sample scores are the
+  // indexer's own floats; the per-wave path keeps the ReLU form (it only places theta)
+  if (FP8 && shared) {  // uniform
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) wv[m][r] *= 0.5f;
+    uint32_t part[kLinParts];
+    const int e0 = lin_split(qi, wv, i, part);
+    if (half == 0) {
+#pragma unroll
+      for (int p = 0; p < kLinParts; ++p) lin_row_store(lin_rows, 8 * (wave >> 1) + 4 * (wave & 1) + p, l32, part[p]);
+    }
+    if (lane == 0) s_e0[wave] = e0;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // visible to the group after the first tile barrier
+  }
   // Wait here, visibly to the compiler, for the query operands (and the segment-count stores):
   // the tiles below arrive by direct loads the compiler does not see, and a wait it placed at
   // the first use of the operands would also drain them. vmcnt(0), other counters untouched.
@@ -1206,17 +1231,24 @@ __global__ __launch_bounds__(512) void topk_theta_kernel(
   // Shared path: tile tl goes to buffer tl % kBufs by direct global->LDS loads (the swizzled
   // layout of key_operand_lds: slot (n, c) holds chunk kswz(n, c)), its key scales beside it
   // (16 per wave).
+  // Addresses are a wave-uniform base plus a 32-bit lane offset recomputed from an opaque copy of
+  // the lane id, so that no per-lane address stays live across the tile loop (a spilled one,
+  // reloaded after tiles were issued, would wait for those tiles too: the wait counts loads in
+  // issue order).
   auto issue_tile = [&](int tl) {
     const int b = tl % kBufs, start = tile_start(tl);
+    const unsigned char* gbase = ki + int64_t(kv0 + start) * kBytes;
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
 #pragma unroll
     for (int j = 0; j < kLoads; ++j) {
       const int f0 = 64 * (kLoads * wave + j);  // this wave's 64 consecutive 16-byte slots
-      const int f = f0 + lane;
+      const int f = f0 + ln;
       const int n = f / kChunks, c = kswz<kChunks>(n, f - n * kChunks);
-      lds_dma16_v(ki + int64_t(kv0 + start + n) * kBytes + c * 16, lds_offset(u.tiles[b] + f0 * 16));
+      lds_dma16_s(uniform_ptr(gbase), uint32_t(n * kBytes + c * 16), lds_offset(u.tiles[b] + f0 * 16));
     }
     if constexpr (FP8) {
-      if (lane < 16) lds_dma4_v(k_scale + kv0 + start + 16 * wave + lane, lds_offset(ks_tiles[b] + 16 * wave));
+      if (ln < 16) lds_dma4_s(k_scale + kv0 + start + 16 * wave, uint32_t(4 * ln), lds_offset(ks_tiles[b] + 16 * wave));
     }
   };
   if (shared) {
@@ -1239,6 +1271,51 @@ __global__ __launch_bounds__(512) void topk_theta_kernel(
       else if (ahead == 1) DSA_TILE_BARRIER_VMCNT(3);
       else DSA_TILE_BARRIER_VMCNT(0);
       if (tl + kBufs - 1 < kSampleTiles) issue_tile(tl + kBufs - 1);
+    }
+    if constexpr (FP8) {
+      if (shared) {
+        // lane-derived LDS addresses come from an opaque copy of the lane id, recomputed every
+        // tile: kept live they are spilled, and a reload would wait for the tiles in flight too
+        int ol = lane;
+        asm volatile("" : "+v"(ol));
+        const int o32 = ol & 31, ohalf = ol >> 5;
+        // waves 0..3: c . k of block `wave` of the tile for the group's 8 rows (lane half h: rows
+        // 2j + h in output rows 8j + 4h + p), times k_scale, published for every wave
+        if (wave < 4) {
+          const int n = 32 * wave + o32;
+          f32x16 L = f32x16{};
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+            L = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(lin_a_operand(lin_rows, o32, ks, ohalf),
+                                                                key_operand_lds<true>(u.tiles[b], n, ks, ohalf), L, 0,
+                                                                0, 0, 127, 0, 127);
+          const float ksn = ks_tiles[b][n];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int q = 2 * j + ohalf;
+            lin_v[q * kLinPitch + n] = lin_combine(L, 4 * j, s_e0[q], ksn);
+          }
+        }
+        DSA_TILE_BARRIER_LDS();
+        // blocks 2pp and 2pp + 1: pair_sum leaves block 2pp's head sum in half 0 and block
+        // 2pp + 1's in half 1, each lane with the key it keeps
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+          float part[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int n = 32 * (2 * pp + h) + o32;
+            f32x16 a0, a1;
+            block_mfma_chains<true>(qa, [&](int ks) { return key_operand_lds<true>(u.tiles[b], n, ks, ohalf); }, a0,
+                                    a1);
+            part[h] = block_abs_part(wv, a0, a1);
+          }
+          const int n = 32 * (2 * pp + ohalf) + o32;
+          const float x = fmaf(pair_sum(part[0], part[1]), ks_tiles[b][n], lin_v[wave * kLinPitch + n]);
+          sk[2 * tl + pp] = order_key(x + 0.f);
+        }
+        continue;
+      }
     }
 #pragma unroll
     for (int pp = 0; pp < 2; ++pp) {
