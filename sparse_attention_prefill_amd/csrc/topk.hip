@@ -1217,7 +1217,8 @@ __global__ __launch_bounds__(512, FP8 ? 4 : 1) void topk_theta_kernel(
     const int e0 = lin_split(qi, wv, i, part);
     if (half == 0) {
 #pragma unroll
-      for (int p = 0; p < kLinParts; ++p) lin_row_store(lin_rows, 8 * (wave >> 1) + 4 * (wave & 1) + p, l32, part[p]);
+      for (int p = 0; p < kLinParts; ++p)
+        lin_row_store(lin_rows, 8 * (wave >> 1) + 4 * (wave & 1) + p, l32, part[p]);
     }
     if (lane == 0) s_e0[wave] = e0;
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // visible to the group after the first tile barrier
@@ -1508,42 +1509,62 @@ __global__ __launch_bounds__(kStreamNT, 1) void topk_refill_kernel(
   __shared__ StreamShared sh;
   // fp8: each wave's copy of the row's split c (kLinParts rows of 128 bytes)
   __shared__ __attribute__((aligned(16))) unsigned char lin_rows[FP8 ? kStreamNT / 64 : 1][FP8 ? kLinParts * kIdxDim : 16];
+  // this workgroup's rows (blockIdx.x + k gridDim.x) that need a recompute, found kStreamNT at a
+  // time with one status read per thread rather than one dependent read per row
+  __shared__ int todo[kStreamNT];
+  __shared__ int n_todo;
   const int lane = threadIdx.x & 63, l32 = lane & 31, half = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   float* srow = scratch + int64_t(blockIdx.x) * sld;
+  auto candidate = [&](int row, QueryView* v) {
+    if (!query_view(cu_q, used_kv, cu_kv, batch, stride, row, v)) return false;
+    const int ev = ratio > 1 ? v->E / ratio : v->E;
+    return v->E >= 1 && ev > fuse_above && ev <= max_vis && v->kv0 >= 0 && int64_t(v->kv0) + ev <= nk;
+  };
 #pragma unroll 1
-  for (int row = blockIdx.x; row < nq; row += gridDim.x) {
-    QueryView v;
-    if (!query_view(cu_q, used_kv, cu_kv, batch, stride, row, &v)) continue;
-    const int ev = ratio > 1 ? v.E / ratio : v.E;
-    if (v.E < 1 || ev <= fuse_above || ev > max_vis || v.kv0 < 0 || int64_t(v.kv0) + ev > nk) continue;
-    if (status[row] != 0) continue;
-    typename IdxOps<FP8>::AOp qa[2][IdxOps<FP8>::kKsteps];
-    float wv[2][16];
-    load_query_operands<FP8>(qi, w, q_scale, row, qa, wv);
-    int e0 = 0;
-    if constexpr (FP8) {
-      // the indexer's fp8 arithmetic: halved weights and the row's split c (every wave its own copy)
+  for (int64_t base = blockIdx.x; base < nq; base += int64_t(gridDim.x) * kStreamNT) {
+    if (threadIdx.x == 0) n_todo = 0;
+    __syncthreads();
+    const int64_t mine = base + int64_t(threadIdx.x) * gridDim.x;
+    QueryView vm;
+    if (mine < nq && candidate(int(mine), &vm) && status[mine] == 0) todo[atomicAdd(&n_todo, 1)] = int(mine);
+    __syncthreads();
+    const int n_rows = n_todo;
+#pragma unroll 1
+    for (int k = 0; k < n_rows; ++k) {
+      const int row = __builtin_amdgcn_readfirstlane(todo[k]);
+      QueryView v;
+      candidate(row, &v);
+      const int ev = ratio > 1 ? v.E / ratio : v.E;
+      typename IdxOps<FP8>::AOp qa[2][IdxOps<FP8>::kKsteps];
+      float wv[2][16];
+      load_query_operands<FP8>(qi, w, q_scale, row, qa, wv);
+      int e0 = 0;
+      if constexpr (FP8) {
+        // the indexer's fp8 arithmetic: halved weights and the row's split c (every wave its own copy)
 #pragma unroll
-      for (int m = 0; m < 2; ++m)
+        for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) wv[m][r] *= 0.5f;
-      uint32_t part[kLinParts];
-      e0 = lin_split(qi, wv, row, part);
-      if (half == 0) {
+          for (int r = 0; r < 16; ++r) wv[m][r] *= 0.5f;
+        uint32_t part[kLinParts];
+        e0 = lin_split(qi, wv, row, part);
+        if (half == 0) {
 #pragma unroll
-        for (int p = 0; p < kLinParts; ++p) lin_row_store(lin_rows[wave], p, l32, part[p]);
+          for (int p = 0; p < kLinParts; ++p) lin_row_store(lin_rows[wave], p, l32, part[p]);
+        }
       }
-    }
 #pragma unroll 1
-    for (int b = wave; 32 * b < ev; b += kStreamNT / 64) {
-      const int p = 32 * b + l32;
-      const float sc = key_score_global<FP8>(qa, wv, lin_rows[FP8 ? wave : 0], e0, ki, k_scale, v.kv0 + min(p, ev - 1));
-      if (half == 0 && p < ev) srow[p] = sc;
+      for (int b = wave; 32 * b < ev; b += kStreamNT / 64) {
+        const int p = 32 * b + l32;
+        const float sc =
+            key_score_global<FP8>(qa, wv, lin_rows[FP8 ? wave : 0], e0, ki, k_scale, v.kv0 + min(p, ev - 1));
+        if (half == 0 && p < ev) srow[p] = sc;
+      }
+      __syncthreads();  // the row's scores are visible to the workgroup
+      stream_select(srow, sld, ev, K, kv_row_base + v.kv0, out + int64_t(row) * (K + window), sh);
+      __syncthreads();  // before the next row overwrites the scratch row and the shared state
     }
-    __syncthreads();  // the row's scores are visible to the workgroup
-    stream_select(srow, sld, ev, K, kv_row_base + v.kv0, out + int64_t(row) * (K + window), sh);
-    __syncthreads();  // before the next row overwrites the scratch row and the shared state
+    __syncthreads();  // every thread has read n_todo and todo before the next batch resets them
   }
 }
 
