@@ -1376,7 +1376,7 @@ struct CandShared {
   int scan[2 * (kCandNT / 64 + 1)];
   int seg_n[64];  // list-segment counts
   uint32_t prefix;
-  int remaining;
+  int remaining, count, n_small;
 };
 
 // Exact top-K of a candidate row from its list (every key >= theta, with its position). The
@@ -1453,10 +1453,40 @@ __global__ __launch_bounds__(kCandNT, 2) void topk_cand_kernel(
     if (lane == 0) {
       sh.prefix = uint32_t(bin);
       sh.remaining = rem;
+      sh.count = cnt;
+      sh.n_small = 0;
     }
   }
+  __syncthreads();
   // lower digits: bits [lo, lo + wb) among the keys whose bits above match the prefix
   int lo = s1;
+  if (s1 > 0 && sh.count <= 64) {  // uniform
+    // The chosen bin holds at most 64 keys: gather their relative keys and let one wave find the
+    // rem-th largest exactly (its ties are then taken by position on emission).
+    const uint32_t pfx = sh.prefix;
+    uint32_t* small_d = sh.hist_r;
+#pragma unroll
+    for (int j = 0; j < kCandEPT; ++j)
+      if (pos[j] >= 0 && (d[j] >> s1) == pfx) small_d[atomicAdd(&sh.n_small, 1)] = d[j];
+    __syncthreads();
+    if (wave == 0) {
+      const int m = sh.n_small, rem = sh.remaining;
+      const uint32_t dl = lane < m ? small_d[lane] : 0u;
+      int n_gt = 0, n_ge = 0;
+      for (int j = 0; j < m; ++j) {
+        const uint32_t dj = __builtin_amdgcn_readlane(dl, j);
+        n_gt += dj > dl;
+        n_ge += dj >= dl;
+      }
+      const uint64_t hit = ballot(lane < m && n_gt < rem && rem <= n_ge);
+      const int l = int(__builtin_ctzll(hit | (1ull << 63)));
+      if (lane == l) {
+        sh.prefix = dl;  // the whole relative key
+        sh.remaining = rem - n_gt;
+      }
+    }
+    lo = 0;
+  }
 #pragma unroll 1
   while (lo > 0) {
     const int wb = min(10, lo);
