@@ -9,15 +9,17 @@
 // Kernels:
 //  * indexer_mfma<bf16|fp8>: 64 heads x 128. A workgroup of 8 waves owns 8 consecutive local
 //    queries (one per wave, whose 64 x 128 query block stays in VGPRs as the MFMA A operand)
-//    and sweeps 256-key tiles of one 2048-key chunk (grid.y) of the union of their causal key
-//    ranges, so even short query batches fill the GPU; tiles are staged in LDS
-//    with direct global->LDS loads (double buffered) and shared by the 8 waves. Each wave
-//    computes the 64 heads x 64 keys logits on 32x32 MFMAs (bf16 32x32x16, or fp8 32x32x64),
-//    then applies ReLU, the head weight and the head sum in fp32: the 32x32 accumulator layout
-//    puts one key per lane and 16 heads per lane, so the head sum is 32 in-lane FMAs plus one
-//    cross-half add. Tiles outside a wave's range are skipped by that wave.
+//    and sweeps 256-key tiles of key chunks (grid.y; at least 4096 keys, longer for long
+//    batches) of the union of their causal key ranges, so even short query batches fill the GPU;
+//    tiles are staged in LDS with direct global->LDS loads (double buffered) and shared by the 8
+//    waves. Each wave computes the logits of 32-key blocks on 32x32 MFMAs (bf16 32x32x16, or fp8
+//    32x32x64), then applies ReLU, the head weight and the head sum in fp32: the 32x32
+//    accumulator layout puts one key per lane and 16 heads per lane, so a lane's half of the head
+//    sum is 32 in-lane FMAs, and one lane swap between the halves finishes two blocks at once.
+//    Tiles outside a wave's range are skipped by that wave.
 //    fp8: q_scale folds into the head weight and k_scale multiplies the head sum (both > 0);
-//    the tile's k_scale values are staged into LDS by the same direct loads as the keys.
+//    the tile's k_scale values are staged into LDS by the same direct loads as the keys, and the
+//    ReLU goes through (x + |x|) / 2 with the linear part on the matrix cores (index_score.h).
 //    Candidate mode (rows longer than the fused-selection bound): instead of writing a score
 //    row, a wave keeps only the scores at or above its row's threshold theta (a 32-bit order
 //    key, see topk.hip) and appends them, with their positions, to its own segment of the row's
